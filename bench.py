@@ -1,0 +1,309 @@
+"""Benchmark of the ragged pack -> attend -> unpack path on one MI355X.
+
+One step = one pass of the whole hot path over one batch: the per-image kept
+token ranks (the cu_seqlens scan), the gather of the kept q/k/v rows, the
+bidirectional ragged attention, and the scatter to the padded output plus the
+CLS rows -- all in ONE launch, `rattn_fused`, called through the Python
+binding.  The default workload is the DeiT-S shape at 80 % token pruning (B=32,
+N=197, H=6, head_dim 64, fp16), the setting the metric "ragged attn seqs/s +
+us/call at 80% pruning" is quoted on.  Inputs are seeded synthetic tensors
+already resident in HBM when the timed region starts.
+
+Printed: ONE JSON line with the throughput (images/s), the fused kernel's
+HIP-event duration and roofline, the CPU oracle timed on this host, and
+(unless --quick) the per-call dispatch floors at batch 1-4 measured from C++
+and the large-configuration kernels against the HBM roof.
+
+Pages on "Dispatch-Aware Ragged Attention for Pruned Vision Transformers"
+(arXiv 2604.15408): the paper abstract (dispatch floor, kernel latency at 80 %
+pruning, serving batch sizes 1-4) and the radpulse.milrad-way.com write-up
+(sections on FlashAttention-2's dispatch ceiling, the Triton kernel and the
+integrated packing pipeline).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+from ragged_variable_length_amd import rattn_fused, rattn_init  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, datasheet
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}  # dense
+ES = {"f32": 4, "f16": 2, "bf16": 2}
+METRIC = "ragged attn seqs/s + us/call at 80% pruning; % of MFMA/HBM roofline"
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work of one launch: what the method must move / compute
+# ---------------------------------------------------------------------------
+def fused_bytes(T: int, B: int, N: int, H: int, dtype: str) -> int:
+    """keep mask read; kept q, k, v rows read once; the padded output (kept
+    rows and zero rows) and the CLS rows written once."""
+    row = H * 64 * ES[dtype]
+    return B * N + 3 * T * row + B * N * row + B * row
+
+
+def attention_bytes(T: int, H: int, dtype: str) -> int:
+    """the attention alone on a flat buffer: q, k, v read and o written once."""
+    return 4 * T * H * 64 * ES[dtype]
+
+
+def attention_flops(lengths, H: int) -> int:
+    """QK^T and PV: 2 * 2 * 64 flops per (query, key) pair per head."""
+    return 4 * 64 * H * sum(L * L for L in lengths)
+
+
+# ---------------------------------------------------------------------------
+# C++ timing helper (host clock around call + sync; no interpreter in the loop)
+# ---------------------------------------------------------------------------
+class BenchStats(ctypes.Structure):
+    _fields_ = [("median_us", ctypes.c_double), ("p5_us", ctypes.c_double),
+                ("p95_us", ctypes.c_double), ("mean_us", ctypes.c_double),
+                ("min_us", ctypes.c_double)]
+
+    def as_dict(self):
+        return {k: round(getattr(self, k), 2) for k, _ in self._fields_}
+
+
+class BenchStep(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_void_p * 3), ("packed", ctypes.c_void_p * 3),
+                ("o", ctypes.c_void_p), ("out_padded", ctypes.c_void_p),
+                ("cls", ctypes.c_void_p), ("keep", ctypes.c_void_p), ("cu", ctypes.c_void_p),
+                ("max_dev", ctypes.c_void_p), ("total_dev", ctypes.c_void_p),
+                ("B", ctypes.c_int), ("N", ctypes.c_int), ("H", ctypes.c_int),
+                ("max_seqlen", ctypes.c_int), ("dtype", ctypes.c_int), ("scale", ctypes.c_float),
+                ("stream", ctypes.c_void_p)]
+
+
+WHAT_FUSED = 2
+_DT_CODE = {"f32": 0, "f16": 1, "bf16": 2}
+_timing = None
+
+
+def timing_lib():
+    global _timing
+    if _timing is None:
+        path = os.path.join(ROOT, "ragged_variable_length_amd", "librattn_bench.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built (run __graft_entry__.build())")
+        lib = ctypes.CDLL(path)
+        P, i32 = ctypes.c_void_p, ctypes.c_int
+        step, stats = ctypes.POINTER(BenchStep), ctypes.POINTER(BenchStats)
+        lib.bench_empty_floor.argtypes = [i32, i32, P, stats]
+        lib.bench_call_floor.argtypes = [step, i32, i32, i32, stats]
+        lib.bench_enqueue_cost.argtypes = [step, i32, i32, stats]
+        lib.bench_graph_floor.argtypes = [step, i32, i32, i32, stats]
+        lib.bench_loop.argtypes = [step, i32, i32]
+        for f in (lib.bench_empty_floor, lib.bench_call_floor, lib.bench_enqueue_cost,
+                  lib.bench_graph_floor, lib.bench_loop):
+            f.restype = i32
+        _timing = lib
+    return _timing
+
+
+class Resident:
+    """A workload moved to the GPU plus its output buffers."""
+
+    def __init__(self, w, stream):
+        self.w = w
+        dev = torch.device("cuda")
+        self.q, self.k, self.v = (t.to(dev) for t in (w.q, w.k, w.v))
+        self.keep = w.keep.to(dev)
+        self.out = torch.empty_like(self.q)
+        self.cls = torch.empty((w.B, w.H, w.D), dtype=self.q.dtype, device=dev)
+        self.stream = stream
+        self.lengths = w.kept_counts
+        self.T = sum(self.lengths)
+        torch.cuda.synchronize()  # inputs resident before any stream uses them
+
+    def step(self):
+        rattn_fused(self.q, self.k, self.v, self.keep, self.w.scale, out_padded=self.out,
+                    cls=self.cls, stream=self.stream)
+
+    def c_step(self) -> BenchStep:
+        s = BenchStep()
+        for i, t in enumerate((self.q, self.k, self.v)):
+            s.src[i] = t.data_ptr()
+        s.out_padded, s.cls = self.out.data_ptr(), self.cls.data_ptr()
+        s.keep = self.keep.data_ptr()
+        s.B, s.N, s.H, s.max_seqlen = self.w.B, self.w.N, self.w.H, self.w.N
+        s.dtype, s.scale = _DT_CODE[self.w.dtype], self.w.scale
+        s.stream = self.stream.cuda_stream
+        return s
+
+
+def dispatch_floors(stream, iters: int, warmup: int) -> dict:
+    """Host call -> completion (C++ steady_clock) at serving batch sizes 1-4,
+    80 % pruning, DeiT-B shape, plus the platform's empty-kernel floor."""
+    lib = timing_lib()
+    st = BenchStats()
+    res = {}
+    if lib.bench_empty_floor(iters, warmup, stream.cuda_stream, ctypes.byref(st)) != 0:
+        raise RuntimeError("bench_empty_floor failed")
+    res["empty_kernel_launch_sync_us"] = st.as_dict()
+    print(f"[bench] empty kernel launch+sync {st.median_us:.2f} us", flush=True)
+    for B in workloads.SWEEP_B:
+        r = Resident(workloads.deit_b_sweep(B, 0.8), stream)
+        cs = r.c_step()
+        row = {"T": r.T}
+        if lib.bench_call_floor(ctypes.byref(cs), WHAT_FUSED, iters, warmup, ctypes.byref(st)):
+            raise RuntimeError("bench_call_floor failed")
+        row["fused_call_sync_us"] = st.as_dict()
+        if lib.bench_enqueue_cost(ctypes.byref(cs), WHAT_FUSED, iters, ctypes.byref(st)):
+            raise RuntimeError("bench_enqueue_cost failed")
+        row["fused_enqueue_us"] = st.as_dict()
+        if lib.bench_graph_floor(ctypes.byref(cs), WHAT_FUSED, iters, warmup, ctypes.byref(st)) == 0:
+            row["fused_graph_replay_sync_us"] = st.as_dict()
+        res[f"deit_b_B{B}_p80"] = row
+        print(f"[bench] dispatch floor B={B}: call+sync {row['fused_call_sync_us']['median_us']} us,"
+              f" enqueue {row['fused_enqueue_us']['median_us']} us", flush=True)
+    return res
+
+
+def kernel_time_us(r: Resident, launches: int, cold: bool, flush_buf=None) -> float:
+    """Median rattn_fused duration from HIP events on the launch stream."""
+    r.step()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(launches):
+        if cold:
+            flush_buf.zero_()  # evict the 256 MB MALL between launches
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(r.stream)
+        r.step()
+        e1.record(r.stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) * 1000.0)
+    times.sort()
+    return times[len(times) // 2]
+
+
+def large_configs(stream, launches: int) -> dict:
+    out = {}
+    flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device="cuda")
+    for name, maker in (("deit_b_384_50pct", workloads.deit_b_384),
+                        ("large_batch_threshold_l2", workloads.large_batch)):
+        w = maker()
+        r = Resident(w, stream)
+        nbytes = fused_bytes(r.T, w.B, w.N, w.H, w.dtype)
+        flops = attention_flops(r.lengths, w.H)
+        row = {"B": w.B, "N": w.N, "H": w.H, "dtype": w.dtype, "T": r.T,
+               "fused_bytes": nbytes, "attn_flops": flops}
+        for cold in (False, True):
+            us = kernel_time_us(r, launches, cold, flush)
+            gbs = nbytes / (us * 1e-6) / 1e9
+            tfl = flops / (us * 1e-6) / 1e12
+            row["cold" if cold else "warm"] = {
+                "us": round(us, 2), "seqs_per_s": round(w.B / (us * 1e-6), 1),
+                "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                "TFLOPs": round(tfl, 2), "mfma_frac": round(tfl / MFMA_PEAK_TFLOPS[w.dtype], 4)}
+        out[name] = row
+        print(f"[bench] {name}: warm {row['warm']['us']} us ({row['warm']['hbm_frac']:.3f} of HBM),"
+              f" cold {row['cold']['us']} us ({row['cold']['hbm_frac']:.3f})", flush=True)
+        del r
+    del flush
+    return out
+
+
+def cpu_baseline(w, budget_s: float) -> dict:
+    """The CPU oracle (plain C, fp64, one thread) on the same workload: whole
+    batches of scan, pack, attention and unpack until the budget is used."""
+    import oracle  # test infrastructure; used only for this reported baseline
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        res = oracle.pipeline(w)
+        oracle.unpack(res["o64"], w.keep, res["cu"])
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(reps * w.B / dt, 2), "unit": "seqs/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} full batch(es) of the {w.name} workload (B={w.B}) through the fp64 "
+                      f"oracle's scan, pack, attention and unpack, {dt:.1f} s on 1 host thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--quick", action="store_true",
+                    help="main metric only: no dispatch floors, no large configs, no CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the path has no "
+              "cross-GPU step and this build runs on a single MI355X; use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    rattn_init()
+    stream = torch.cuda.current_stream()
+
+    w = workloads.deit_s()
+    r = Resident(w, stream)
+    print(f"[bench] workload {w.name}: B={w.B} N={w.N} H={w.H} {w.dtype} T={r.T}", flush=True)
+    for _ in range(args.warmup):
+        r.step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        r.step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1000.0 / K
+    kern_us = sum(a.elapsed_time(b) for a, b in ev) * 1000.0 / K
+    nbytes = fused_bytes(r.T, w.B, w.N, w.H, w.dtype)
+    achieved = nbytes / (kern_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": "rattn_fused", "achieved": round(achieved, 2),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
+                "traffic": None, "bytes_per_launch": nbytes, "avg_launch_us": round(kern_us, 3)}
+
+    line = {
+        "metric": METRIC, "value": round(w.B / (ms_per_step / 1000.0), 1), "unit": "seqs/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": "deit_s_80pct", "B": w.B, "N": w.N, "H": w.H, "head_dim": 64,
+                   "total_tokens": r.T, "max_seqlen_arg": w.N,
+                   "step": "rattn_fused (scan + pack + attention + unpack/CLS, one launch) "
+                           "via the Python binding"},
+        "us_per_step": round(ms_per_step * 1000.0, 2),
+        "kernel_avg_us": {"rattn_fused": round(kern_us, 3)},
+        "attn_flops": attention_flops(r.lengths, w.H),
+        "roofline": roofline,
+    }
+    if not args.quick:
+        side = torch.cuda.Stream()  # graph capture needs a non-default stream
+        line["dispatch_floor"] = dispatch_floors(side, iters=1000, warmup=100)
+        line["large_configs"] = large_configs(stream, launches=20)
+    if not args.quick and not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,14 @@
+"""MI355X-native pack -> attend -> unpack for token-pruned Vision Transformers.
+
+The work runs in librattn.so (hand-written HIP kernels for gfx950 behind a C
+ABI declared in include/rattn.h).  This package is its Python binding:
+`rattn_pack`, `rattn_forward`, `rattn_unpack` and `rattn_fused` have the C
+entry points' names and only marshal arguments; `RaggedPipeline` owns the device buffers
+(allocated once, through torch) for repeated calls of the three.
+"""
+from ._binding import (LIB_PATH, RattnError, load, rattn_forward, rattn_fused, rattn_init,
+                       rattn_pack, rattn_unpack, status_string)
+from .pipeline import RaggedPipeline
+
+__all__ = ["LIB_PATH", "RattnError", "RaggedPipeline", "load", "rattn_forward", "rattn_fused",
+           "rattn_init", "rattn_pack", "rattn_unpack", "status_string"]

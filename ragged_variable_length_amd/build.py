@@ -1,0 +1,59 @@
+"""Build librattn.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc."""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "librattn.so")
+SOURCES = ["api.hip", "pack.hip", "attention.hip"]
+# host-side timing loops used by bench.py (links librattn.so; not product ABI)
+BENCH_LIB = os.path.join(HERE, "librattn_bench.so")
+BENCH_SOURCES = ["bench_host.hip"]
+
+# Device-code flags: gfx950 only; packed-fp32 instruction selection off (the
+# compiler would otherwise form v_pk_* float ops on its own).
+DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
+                "-packed-fp32-ops"]
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found (ROCm is required to build librattn.so)")
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile librattn.so and librattn_bench.so next to this file (always rebuilds)."""
+    _compile(LIB, SOURCES, [], verbose, extra_flags)
+    _compile(BENCH_LIB, BENCH_SOURCES, ["-L", HERE, "-lrattn", "-Wl,-rpath,$ORIGIN"],
+             verbose, extra_flags)
+    return LIB
+
+
+def _compile(out: str, sources, link_flags, verbose: bool, extra_flags) -> None:
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *DEVICE_FLAGS, "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC,
+           *extra_flags, "-o", tmp, *[os.path.join(CSRC, s) for s in sources], *link_flags]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # the host pass warns that it does not know the packed-fp32 feature: harmless
+    noise = "is not a recognized feature for this target"
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs), file=sys.stderr)
+    os.replace(tmp, out)
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

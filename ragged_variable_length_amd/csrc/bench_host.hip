@@ -1,0 +1,183 @@
+// bench_host.hip -- host-side timing of librattn's C ABI for the benchmark.
+// Built into librattn_bench.so; NOT part of the product ABI (include/rattn.h).
+//
+// The quantity the pages put first is the per-call dispatch floor: host call
+// to completion at ViT sizes, where launch overhead exceeds the compute (paper
+// abstract; radpulse.milrad-way.com write-up, sections on FlashAttention-2's
+// 62 us ceiling and the 40 us Triton kernel).  These loops time it from C++
+// with std::chrono::steady_clock, so that no interpreter sits in the loop:
+//   * empty-kernel launch + hipStreamSynchronize: the platform's floor;
+//   * rattn_forward + sync, the whole pack -> forward -> unpack step + sync, and
+//     the one-launch rattn_fused + sync;
+//   * the same step replayed from a captured hipGraph + sync;
+//   * enqueue-only cost of the calls (no sync inside the timed span).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <vector>
+
+#include "rattn.h"
+
+extern "C" {
+
+typedef struct bench_stats {
+    double median_us, p5_us, p95_us, mean_us, min_us;
+} bench_stats;
+
+typedef struct bench_step {
+    const void *src[3];   // padded q, k, v [B, N, H, 64]
+    void *packed[3];      // flat q, k, v [>= T, H, 64]
+    void *o;              // flat attention output
+    void *out_padded;     // [B, N, H, 64] (nullable)
+    void *cls;            // [B, H, 64] (nullable)
+    const uint8_t *keep;  // [B, N]
+    int32_t *cu;          // [B+1]
+    int32_t *max_dev;     // nullable
+    int32_t *total_dev;   // nullable
+    int B, N, H, max_seqlen, dtype;
+    float scale;
+    void *stream;
+} bench_step;
+
+}  // extern "C"
+
+namespace {
+
+__global__ void empty_kernel() {}
+
+using clk = std::chrono::steady_clock;
+
+void summarize(std::vector<double> &v, bench_stats *s) {
+    std::sort(v.begin(), v.end());
+    const size_t n = v.size();
+    auto at = [&](double f) { return v[std::min(n - 1, (size_t)(f * (n - 1) + 0.5))]; };
+    double sum = 0;
+    for (double x : v) sum += x;
+    s->median_us = at(0.5);
+    s->p5_us = at(0.05);
+    s->p95_us = at(0.95);
+    s->mean_us = sum / n;
+    s->min_us = v[0];
+}
+
+rattn_status do_forward(const bench_step *a) {
+    return rattn_forward(a->packed[0], a->packed[1], a->packed[2], a->o, a->cu, a->B,
+                         a->max_seqlen, a->H, RATTN_HEAD_DIM, a->scale, (rattn_dtype)a->dtype,
+                         a->stream);
+}
+
+rattn_status do_step(const bench_step *a) {
+    rattn_status s = rattn_pack(a->src, a->packed, 3, a->keep, a->B, a->N, a->H * RATTN_HEAD_DIM,
+                                (rattn_dtype)a->dtype, a->cu, a->max_dev, a->total_dev, a->stream);
+    if (s != RATTN_OK) return s;
+    s = do_forward(a);
+    if (s != RATTN_OK) return s;
+    return rattn_unpack(a->o, a->out_padded, a->cls, a->keep, a->cu, a->B, a->N,
+                        a->H * RATTN_HEAD_DIM, (rattn_dtype)a->dtype, a->stream);
+}
+
+rattn_status do_fused(const bench_step *a) {
+    return rattn_fused(a->src[0], a->src[1], a->src[2], a->keep, a->out_padded, a->cls, a->B, a->N,
+                       a->H, RATTN_HEAD_DIM, a->max_seqlen, a->scale, (rattn_dtype)a->dtype,
+                       a->stream);
+}
+
+// what = 0: rattn_forward; 1: rattn_pack + rattn_forward + rattn_unpack;
+// 2: rattn_fused (the same pack -> attend -> unpack in one launch).
+rattn_status run(const bench_step *a, int what) {
+    return what == 0 ? do_forward(a) : what == 1 ? do_step(a) : do_fused(a);
+}
+
+}  // namespace
+
+extern "C" {
+
+// Empty kernel launch + stream sync, `iters` times after `warmup`.
+int bench_empty_floor(int iters, int warmup, void *stream, bench_stats *out) {
+    hipStream_t s = (hipStream_t)stream;
+    std::vector<double> t;
+    t.reserve(iters);
+    for (int i = 0; i < warmup + iters; ++i) {
+        auto t0 = clk::now();
+        hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, s);
+        if (hipStreamSynchronize(s) != hipSuccess) return -1;
+        auto t1 = clk::now();
+        if (i >= warmup) t.push_back(std::chrono::duration<double, std::micro>(t1 - t0).count());
+    }
+    summarize(t, out);
+    return 0;
+}
+
+// Each iteration: host call(s) + hipStreamSynchronize, timed on the host.
+int bench_call_floor(const bench_step *a, int what, int iters, int warmup, bench_stats *out) {
+    hipStream_t s = (hipStream_t)a->stream;
+    std::vector<double> t;
+    t.reserve(iters);
+    for (int i = 0; i < warmup + iters; ++i) {
+        auto t0 = clk::now();
+        if (run(a, what) != RATTN_OK) return -2;
+        if (hipStreamSynchronize(s) != hipSuccess) return -1;
+        auto t1 = clk::now();
+        if (i >= warmup) t.push_back(std::chrono::duration<double, std::micro>(t1 - t0).count());
+    }
+    summarize(t, out);
+    return 0;
+}
+
+// Host time of the call(s) alone (enqueue, no sync inside the span); the
+// stream is drained every 64 iterations outside the timed spans.
+int bench_enqueue_cost(const bench_step *a, int what, int iters, bench_stats *out) {
+    hipStream_t s = (hipStream_t)a->stream;
+    std::vector<double> t;
+    t.reserve(iters);
+    for (int i = 0; i < iters; ++i) {
+        auto t0 = clk::now();
+        if (run(a, what) != RATTN_OK) return -2;
+        auto t1 = clk::now();
+        t.push_back(std::chrono::duration<double, std::micro>(t1 - t0).count());
+        if ((i & 63) == 63 && hipStreamSynchronize(s) != hipSuccess) return -1;
+    }
+    if (hipStreamSynchronize(s) != hipSuccess) return -1;
+    summarize(t, out);
+    return 0;
+}
+
+// Enqueue `steps` calls back to back with no synchronisation (the caller
+// brackets it with its own synchronisation and clock).
+int bench_loop(const bench_step *a, int what, int steps) {
+    for (int i = 0; i < steps; ++i)
+        if (run(a, what) != RATTN_OK) return -2;
+    return 0;
+}
+
+// The same call(s) captured once into a hipGraph and replayed: launch + sync
+// per iteration.  The capture stream must not be the legacy default stream.
+int bench_graph_floor(const bench_step *a, int what, int iters, int warmup, bench_stats *out) {
+    hipStream_t s = (hipStream_t)a->stream;
+    if (!s) return -3;
+    hipGraph_t g = nullptr;
+    hipGraphExec_t ge = nullptr;
+    if (hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal) != hipSuccess) return -1;
+    rattn_status st = run(a, what);
+    if (hipStreamEndCapture(s, &g) != hipSuccess || st != RATTN_OK) return -2;
+    if (hipGraphInstantiate(&ge, g, nullptr, nullptr, 0) != hipSuccess) return -1;
+    std::vector<double> t;
+    t.reserve(iters);
+    int rc = 0;
+    for (int i = 0; i < warmup + iters; ++i) {
+        auto t0 = clk::now();
+        if (hipGraphLaunch(ge, s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess) {
+            rc = -1;
+            break;
+        }
+        auto t1 = clk::now();
+        if (i >= warmup) t.push_back(std::chrono::duration<double, std::micro>(t1 - t0).count());
+    }
+    (void)hipGraphExecDestroy(ge);
+    (void)hipGraphDestroy(g);
+    if (rc == 0) summarize(t, out);
+    return rc;
+}
+
+}  // extern "C"

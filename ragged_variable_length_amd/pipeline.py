@@ -1,0 +1,54 @@
+"""Device buffers for repeated pack -> attend -> unpack calls.
+
+Pages on "Dispatch-Aware Ragged Attention for Pruned Vision Transformers"
+(arXiv 2604.15408), radpulse.milrad-way.com write-up, section on the
+integrated packing pipeline: cu_seqlens, pack, attend, CLS extract.
+
+Buffers are sized from (B, N, H) once, with capacity B*N rows for the flat
+tensors, so no call needs the kept-token count on the host: there is no
+device-to-host copy and no allocation inside `run`.  Every step is one of the
+three C entry points; nothing here computes.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._binding import rattn_forward, rattn_pack, rattn_unpack
+
+
+class RaggedPipeline:
+    def __init__(self, B: int, N: int, H: int, dtype: torch.dtype, device="cuda",
+                 head_dim: int = 64, want_padded: bool = True, want_cls: bool = True):
+        self.B, self.N, self.H, self.D = B, N, H, head_dim
+        self.dtype = dtype
+        dev = torch.device(device)
+        cap = max(1, B * N)
+        shape = (cap, H, head_dim)
+        self.pq = torch.empty(shape, dtype=dtype, device=dev)
+        self.pk = torch.empty(shape, dtype=dtype, device=dev)
+        self.pv = torch.empty(shape, dtype=dtype, device=dev)
+        self.po = torch.empty(shape, dtype=dtype, device=dev)
+        self.cu = torch.empty(B + 1, dtype=torch.int32, device=dev)
+        self.max_seqlen_dev = torch.empty(1, dtype=torch.int32, device=dev)
+        self.total_dev = torch.empty(1, dtype=torch.int32, device=dev)
+        self.out = (torch.empty((B, N, H, head_dim), dtype=dtype, device=dev)
+                    if want_padded else None)
+        self.cls = torch.empty((B, H, head_dim), dtype=dtype, device=dev) if want_cls else None
+
+    def pack(self, q, k, v, keep, stream=None):
+        rattn_pack((q, k, v), (self.pq, self.pk, self.pv), keep, self.cu,
+                   self.max_seqlen_dev, self.total_dev, stream=stream)
+
+    def attend(self, scale: float, max_seqlen: int | None = None, stream=None):
+        ms = self.N if max_seqlen is None else max_seqlen
+        rattn_forward(self.pq, self.pk, self.pv, self.po, self.cu, ms, scale, stream=stream)
+
+    def unpack(self, keep, stream=None):
+        rattn_unpack(self.po, keep, self.cu, dst_padded=self.out, cls=self.cls, stream=stream)
+
+    def run(self, q, k, v, keep, scale: float, max_seqlen: int | None = None, stream=None):
+        """q, k, v: padded [B, N, H, 64] device tensors; keep: uint8 [B, N]."""
+        self.pack(q, k, v, keep, stream)
+        self.attend(scale, max_seqlen, stream)
+        self.unpack(keep, stream)
+        return self.out, self.cls

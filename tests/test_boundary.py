@@ -1,0 +1,150 @@
+"""The C ABI boundary on the host (no GPU needed, no kernel launched).
+
+Checks that librattn.so loads, exports every entry point include/rattn.h
+declares, and rejects invalid arguments on the host before any HIP call, with
+the documented status codes.  Fake device addresses are only passed where the
+argument check must fail first, so nothing is ever dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import ragged_variable_length_amd as rv
+from ragged_variable_length_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rattn.h")
+
+OK, INVALID, UNSUPPORTED, NO_DEVICE, HIP = 0, 1, 2, 3, 4
+F32, F16, BF16 = 0, 1, 2
+A = 0x10000  # a 16-byte-aligned fake device address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rattn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return rv.load()
+
+
+def test_header_declares_the_three_path_calls():
+    names = declared_functions()
+    for n in ("rattn_pack", "rattn_forward", "rattn_unpack", "rattn_init",
+              "rattn_status_string", "rattn_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.rattn_version() >> 16 == 1
+    for code in (OK, INVALID, UNSUPPORTED, NO_DEVICE, HIP, 99):
+        s = rv.status_string(code)
+        assert isinstance(s, str) and s
+
+
+def _fwd(lib, q=A, k=A, v=A, o=A, cu=A, B=2, ms=10, H=2, D=64, scale=0.125, dt=BF16):
+    return lib.rattn_forward(q, k, v, o, cu, B, ms, H, D, ctypes.c_float(scale), dt, None)
+
+
+def test_forward_argument_checks(lib):
+    assert _fwd(lib, D=32) == UNSUPPORTED
+    assert _fwd(lib, D=128) == UNSUPPORTED
+    assert _fwd(lib, dt=7) == INVALID
+    assert _fwd(lib, B=-1) == INVALID
+    assert _fwd(lib, H=0) == INVALID
+    assert _fwd(lib, ms=-3) == INVALID
+    assert _fwd(lib, scale=float("nan")) == INVALID
+    assert _fwd(lib, scale=float("inf")) == INVALID
+    assert _fwd(lib, q=None) == INVALID
+    assert _fwd(lib, o=None) == INVALID
+    assert _fwd(lib, cu=None) == INVALID
+    assert _fwd(lib, k=A + 8) == INVALID  # not 16-byte aligned
+    assert _fwd(lib, cu=A + 2) == INVALID  # not 4-byte aligned
+    # nothing to do: succeeds without touching the device or the pointers
+    assert _fwd(lib, B=0, q=None, k=None, v=None, o=None, cu=None) == OK
+    assert _fwd(lib, ms=0, q=None, k=None, v=None, o=None, cu=None) == OK
+
+
+def _pack(lib, n=3, src=(A, A, A), dst=(A, A, A), keep=A, B=2, N=197, row=384, dt=BF16, cu=A,
+          mx=None, tot=None):
+    sa = (ctypes.c_void_p * 3)(*src) if src is not None else None
+    da = (ctypes.c_void_p * 3)(*dst) if dst is not None else None
+    return lib.rattn_pack(sa, da, n, keep, B, N, row, dt, cu, mx, tot, None)
+
+
+def test_pack_argument_checks(lib):
+    assert _pack(lib, n=0) == INVALID
+    assert _pack(lib, n=4) == INVALID
+    assert _pack(lib, src=None) == INVALID
+    assert _pack(lib, dst=None) == INVALID
+    assert _pack(lib, src=(A, None, A)) == INVALID
+    assert _pack(lib, dst=(A, A, A + 4)) == INVALID
+    assert _pack(lib, keep=None) == INVALID
+    assert _pack(lib, keep=A + 1) == INVALID
+    assert _pack(lib, cu=None) == INVALID
+    assert _pack(lib, cu=A + 1) == INVALID
+    assert _pack(lib, mx=A + 2) == INVALID
+    assert _pack(lib, tot=A + 2) == INVALID
+    assert _pack(lib, B=-1) == INVALID
+    assert _pack(lib, N=0) == INVALID
+    assert _pack(lib, B=1 << 20, N=1 << 12) == INVALID  # B*N beyond int32
+    assert _pack(lib, row=0) == INVALID
+    assert _pack(lib, row=3, dt=F16) == INVALID  # 6-byte rows are not 16-byte multiples
+    assert _pack(lib, dt=9) == INVALID
+
+
+def _unpack(lib, src=A, dst=A, cls=A, keep=A, cu=A, B=2, N=197, row=384, dt=BF16):
+    return lib.rattn_unpack(src, dst, cls, keep, cu, B, N, row, dt, None)
+
+
+def test_unpack_argument_checks(lib):
+    assert _unpack(lib, dst=None, cls=None) == INVALID
+    assert _unpack(lib, src=None) == INVALID
+    assert _unpack(lib, keep=None) == INVALID
+    assert _unpack(lib, cu=None) == INVALID
+    assert _unpack(lib, src=A + 8) == INVALID
+    assert _unpack(lib, dst=A + 8) == INVALID
+    assert _unpack(lib, cls=A + 8) == INVALID
+    assert _unpack(lib, N=0) == INVALID
+    assert _unpack(lib, row=5, dt=F32) == INVALID
+    assert _unpack(lib, B=0, src=None, keep=None, cu=None) == OK
+
+
+def test_valid_call_without_device_reports_no_device(lib):
+    if lib.rattn_init() == OK:
+        pytest.skip("a gfx950 device is present; this checks the device-less path")
+    assert lib.rattn_init() == NO_DEVICE
+    assert _fwd(lib) == NO_DEVICE
+    assert _pack(lib) == NO_DEVICE
+    assert _unpack(lib) == NO_DEVICE
+
+
+def test_binding_refuses_host_tensors():
+    x = torch.zeros((2, 4, 2, 64), dtype=torch.bfloat16)
+    keep = torch.ones((2, 4), dtype=torch.uint8)
+    cu = torch.zeros(3, dtype=torch.int32)
+    flat = torch.zeros((8, 2, 64), dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        rv.rattn_pack([x], [flat], keep, cu)
+    with pytest.raises(TypeError):
+        rv.rattn_forward(flat, flat, flat, flat, cu, 4, 0.125)
+    with pytest.raises(TypeError):
+        rv.rattn_unpack(flat, keep, cu, dst_padded=x)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _binding.load()

@@ -1,0 +1,250 @@
+"""Parity of the one-launch path (rattn_fused, through the C ABI) with the CPU
+oracle, on MI355X.
+
+rattn_fused reads padded q/k/v and the keep mask and writes the padded output
+and the CLS rows directly.  Checked: pruned output rows are exactly zero; the
+kept rows, gathered in (b, n) order, match the oracle's attention within the
+tolerances of `_gpu_util` (fp32 1e-4, fp16 2e-3, bf16 1e-2 max-abs on
+unit-normal inputs; the 384 px workload against the derived rounding bound);
+CLS rows are bitwise the output rows (b, 0); results do not depend on the
+max_seqlen bound, on the contents of pruned input rows, on other images, or on
+the run.  The five named workloads run at full size in the launch
+configuration the benchmark times (max_seqlen = N); at the two largest the
+oracle computes sampled rows one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests._gpu_util import FLAT_TOL, UNIT_ROUNDOFF, bits, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+POISON = 0xA5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import ragged_variable_length_amd as rv
+    rv.rattn_init()
+
+
+def run_fused(w, max_seqlen=None, poison_pruned=False, want_out=True, want_cls=True,
+              stream=None):
+    """One rattn_fused call; returns CPU copies of (out, cls)."""
+    import ragged_variable_length_amd as rv
+    dev = torch.device("cuda")
+    q, k, v = (t.clone() for t in (w.q, w.k, w.v))
+    if poison_pruned:
+        pruned = w.keep == 0
+        for t in (q, k, v):
+            t[pruned] = float("nan")
+    q, k, v = (t.to(dev) for t in (q, k, v))
+    keep = w.keep.to(dev)
+    out = torch.empty_like(q) if want_out else None
+    cls = torch.empty((w.B, w.H, w.D), dtype=q.dtype, device=dev) if want_cls else None
+    for t in (out, cls):
+        if t is not None:
+            t.view(torch.uint8).fill_(POISON)
+    rv.rattn_fused(q, k, v, keep, w.scale, out_padded=out, cls=cls, max_seqlen=max_seqlen,
+                   stream=stream)
+    torch.cuda.synchronize()
+    return (None if out is None else out.cpu()), (None if cls is None else cls.cpu())
+
+
+def kept_rows(out, keep):
+    """Kept rows of a padded output, in (b, n) order (bitwise gather)."""
+    return oracle.pack(out, keep)
+
+
+def check(w, out, cls, o64, absw, rows=None, flat=True):
+    keep = w.keep.numpy() != 0
+    ob = bits(out)
+    assert not ob[~keep].any(), "pruned output rows are not all-zero bytes"
+    cb = bits(cls)
+    for b in range(w.B):
+        assert np.array_equal(cb[b], ob[b, 0]), f"CLS row of image {b} differs from out[b, 0]"
+    got = oracle.widen(kept_rows(out, w.keep), w.dtype).reshape(-1, w.H, w.D)
+    if rows is not None:
+        got = got[rows]
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - o64)
+    bound = FLAT_TOL[w.dtype] + 2.0 * UNIT_ROUNDOFF[w.dtype] * (np.abs(o64) + absw)
+    e, r = float(err.max()) if err.size else 0.0, float((err / bound).max()) if err.size else 0.0
+    say(f"{w.name}: max|err|={e:.3e} err/bound={r:.3f}")
+    if flat:
+        assert e <= FLAT_TOL[w.dtype], e
+    assert r <= 1.0, r
+
+
+def full(w, flat=True, **kw):
+    say(f"{w.name}: B={w.B} N={w.N} H={w.H} {w.dtype} T={w.total_kept}")
+    ref = oracle.pipeline(w, want_absw=True)
+    out, cls = run_fused(w, **kw)
+    check(w, out, cls, ref["o64"], ref["absw"], flat=flat)
+    return out, cls, ref
+
+
+# ---------------------------------------------------------------------------
+# the named workloads, full size, max_seqlen = N
+# ---------------------------------------------------------------------------
+def test_fused_tiny_fp32():
+    full(workloads.tiny())
+
+
+def test_fused_deit_s_80pct_fp16():
+    full(workloads.deit_s())
+
+
+@pytest.mark.parametrize("B,p,exact", workloads.sweep_points())
+def test_fused_deit_b_sweep_bf16(B, p, exact):
+    full(workloads.deit_b_sweep(B, p, exact_unpruned=exact))
+
+
+def _sampled(w, nrows, flat):
+    say(f"{w.name}: B={w.B} N={w.N} H={w.H} {w.dtype} T={w.total_kept} (sampled rows)")
+    out, cls = run_fused(w)
+    cu, _, T = oracle.scan(w.keep)
+    pq, pk, pv = (oracle.pack(t, w.keep) for t in (w.q, w.k, w.v))
+    rows = sample_rows(cu, nrows, seed=w.seed)
+    o64, absw = oracle.attention(*(oracle.widen(t, w.dtype).reshape(T, w.H, w.D)
+                                   for t in (pq, pk, pv)), cu, w.scale, rows=rows,
+                                 want_absw=True)
+    check(w, out, cls, o64, absw, rows=rows, flat=flat)
+
+
+def test_fused_deit_b_384_50pct_outliers_bf16():
+    _sampled(workloads.deit_b_384(), nrows=160, flat=False)
+
+
+def test_fused_large_batch_threshold_bf16():
+    _sampled(workloads.large_batch(), nrows=400, flat=True)
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+def _keep_with_lengths(lengths, N, seed):
+    g = torch.Generator().manual_seed(seed)
+    keep = torch.zeros((len(lengths), N), dtype=torch.uint8)
+    for b, L in enumerate(lengths):
+        keep[b, torch.randperm(N, generator=g)[:L]] = 1
+    return keep
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_fused_ragged_tails(dtype):
+    lengths = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200]
+    keep = _keep_with_lengths(lengths, 200, seed=3)
+    full(workloads.custom(len(lengths), 200, 2, dtype, keep=keep, seed=11,
+                          name=f"tails_{dtype}"), flat=False)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_fused_length_one_returns_v_row(dtype):
+    B, N = 6, 197
+    keep = torch.zeros((B, N), dtype=torch.uint8)
+    keep[:, 0] = 1
+    keep[3, 0] = 0
+    keep[3, 77] = 1  # one kept patch, CLS pruned
+    w = workloads.custom(B, N, 3, dtype, keep=keep, seed=12, name=f"len1_{dtype}")
+    out, cls, ref = full(w, flat=False)
+    assert np.array_equal(bits(kept_rows(out, w.keep)), ref["v"].view(bits(out).dtype))
+
+
+def test_fused_empty_images_and_pruned_cls():
+    B, N = 5, 40
+    keep = torch.zeros((B, N), dtype=torch.uint8)
+    keep[1, [3, 9, 10]] = 1
+    keep[3, :] = 1
+    out, cls, _ = full(workloads.custom(B, N, 2, "bf16", keep=keep, seed=13, name="empty"),
+                       flat=False)
+    assert not cls[[0, 1, 2, 4]].view(torch.int16).any()
+
+
+def test_fused_everything_pruned():
+    B, N = 3, 50
+    w = workloads.custom(B, N, 2, "bf16", keep=torch.zeros((B, N), dtype=torch.uint8), seed=14)
+    say("every token pruned")
+    out, cls = run_fused(w)
+    assert not out.view(torch.int16).any() and not cls.view(torch.int16).any()
+    out0, cls0 = run_fused(w, max_seqlen=0)
+    assert not out0.view(torch.int16).any() and not cls0.view(torch.int16).any()
+
+
+@pytest.mark.parametrize("N", [577, 1100, 2048])
+def test_fused_long_sequences(N):
+    keep = torch.ones((2, N), dtype=torch.uint8)
+    keep[1, N // 3:] = 0
+    full(workloads.custom(2, N, 2, "bf16", keep=keep, seed=15, name=f"long_{N}"), flat=False)
+
+
+@pytest.mark.parametrize("B,N", [(1, 1), (3, 5), (700, 7)])
+def test_fused_small_rows(B, N):
+    full(workloads.custom(B, N, 1, "bf16", p_keep=0.6, seed=16 + N, name=f"small_{B}x{N}"),
+         flat=False)
+
+
+def test_fused_max_seqlen_bound_does_not_change_bits():
+    w = workloads.deit_s()
+    say("max_seqlen exact vs N vs 4N")
+    a = run_fused(w, max_seqlen=max(w.kept_counts))
+    b = run_fused(w, max_seqlen=w.N)
+    c = run_fused(w, max_seqlen=4 * w.N)
+    for x, y in ((a, b), (a, c)):
+        assert np.array_equal(bits(x[0]), bits(y[0])) and np.array_equal(bits(x[1]), bits(y[1]))
+
+
+def test_fused_poisoned_pruned_rows_do_not_leak():
+    w = workloads.deit_b_sweep(4, 0.5)
+    say("NaN-poisoned pruned rows")
+    a = run_fused(w)
+    b = run_fused(w, poison_pruned=True)
+    assert np.array_equal(bits(a[0]), bits(b[0])) and np.array_equal(bits(a[1]), bits(b[1]))
+
+
+def test_fused_run_to_run_determinism():
+    w = workloads.large_batch(B=64)
+    say("determinism")
+    a, b = run_fused(w), run_fused(w)
+    assert np.array_equal(bits(a[0]), bits(b[0])) and np.array_equal(bits(a[1]), bits(b[1]))
+
+
+def test_fused_cross_image_isolation():
+    w = workloads.deit_b_sweep(4, 0.25)
+    say("isolation")
+    a = run_fused(w)
+    w.k[2] = -w.k[2]
+    w.v[2] = w.v[2] * 2
+    b = run_fused(w)
+    others = [0, 1, 3]
+    assert np.array_equal(bits(a[0])[others], bits(b[0])[others])
+    assert not np.array_equal(bits(a[0])[2], bits(b[0])[2])
+
+
+def test_fused_cls_only_matches_full():
+    w = workloads.deit_b_sweep(4, 0.8)
+    say("CLS rows only")
+    _, cls_full = run_fused(w)
+    out_none, cls_only = run_fused(w, want_out=False)
+    assert out_none is None
+    assert np.array_equal(bits(cls_only), bits(cls_full))
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, 0.5])
+def test_fused_unusual_scales(scale):
+    full(workloads.custom(4, 90, 2, "bf16", p_keep=0.7, seed=17, scale=scale,
+                          name=f"scale_{scale}"), flat=False)
+
+
+def test_fused_side_stream():
+    w = workloads.deit_b_sweep(2, 0.8)
+    s = torch.cuda.Stream()
+    say("non-default stream")
+    ref = oracle.pipeline(w, want_absw=True)
+    with torch.cuda.stream(s):
+        out, cls = run_fused(w, stream=s)
+    check(w, out, cls, ref["o64"], ref["absw"])
