@@ -23,8 +23,11 @@ def say(msg: str) -> None:
     sys.stdout.flush()
 
 
-def bits(t: torch.Tensor) -> np.ndarray:
-    """Storage bits of a tensor as an integer numpy array (CPU copy)."""
+def bits(t) -> np.ndarray:
+    """Storage bits of a tensor or array as an integer numpy array (CPU copy)."""
+    if isinstance(t, np.ndarray):
+        a = np.ascontiguousarray(t)
+        return a.view({1: np.uint8, 2: np.int16, 4: np.int32, 8: np.int64}[a.dtype.itemsize])
     t = t.detach().cpu().contiguous()
     if t.element_size() == 2:
         return t.view(torch.int16).numpy()
