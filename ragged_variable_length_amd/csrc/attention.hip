@@ -43,6 +43,8 @@
 //    each (image, head) also writes zeros to the pruned rows and the CLS row.
 // The float32 path has the same structure on v_mfma_f32_16x16x4_f32 with
 // 32-key chunks, row-padded LDS and probabilities kept in float32.
+#include <algorithm>
+
 #include "internal.h"
 
 namespace rattn {
@@ -65,12 +67,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 template <typename T> struct Mma;
 template <> struct Mma<__bf16> {
     typedef bf16x8 v8;
+    static constexpr uint32_t kOnePair = 0x3F803F80u;  // two bf16 1.0
     static __device__ __forceinline__ f32x4 run(v8 a, v8 b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     }
 };
 template <> struct Mma<_Float16> {
     typedef f16x8 v8;
+    static constexpr uint32_t kOnePair = 0x3C003C00u;  // two fp16 1.0
     static __device__ __forceinline__ f32x4 run(v8 a, v8 b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
     }
@@ -98,19 +102,6 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
            ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// (image, head, query tile) of this workgroup; false if the id is padding.
-__device__ __forceinline__ bool decode_tile(int B, int H, int ntiles, int *b, int *h,
-                                            int *tile) {
-    const int id = blockIdx.x;
-    const int xcd = id & 7, local = id >> 3;
-    const int pair = (local / ntiles) * 8 + xcd;
-    *tile = local - (local / ntiles) * ntiles;
-    if (pair >= B * H) return false;
-    *b = pair / H;
-    *h = pair - *b * H;
-    return true;
-}
-
 // Element offset of the 64-element head slice of kept row r of one
 // (image, head), in the flat ragged buffer or in the padded tensor.
 struct FlatRows {
@@ -123,200 +114,293 @@ struct PaddedRows {
     __device__ __forceinline__ int64_t at(int r) const { return base + (int64_t)pos[r] * rs; }
 };
 
-// 16-byte piece p of LDS row `row` (128-byte rows), XOR-swizzled.
-__device__ __forceinline__ int swz(int row, int piece) { return row * 64 + 8 * (piece ^ (row & 7)); }
+// LDS tiles of the 16-bit path are 64 rows x 128 bytes, written by
+// global->LDS DMA (each lane's 16 bytes land at base + 16*lane) and read as
+// MFMA operands.  The 16-byte pieces of each row are XOR-permuted so that the
+// reads hit distinct banks: K rows (read as 16-byte row slices) by
+// (row ^ row>>3) & 7, V rows (read transposed, 8 bytes per lane) by
+// 2 * ((row ^ row>>1) & 3).  A lane fetches from global memory whichever piece
+// belongs in its LDS slot, so the permutation costs nothing at staging time.
+__device__ __forceinline__ int kpiece(int row, int p) { return p ^ ((row ^ (row >> 3)) & 7); }
+__device__ __forceinline__ int vpiece(int row, int p) { return p ^ (((row ^ (row >> 1)) & 3) << 1); }
+
+#define RATTN_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing 8-byte LDS read (ds_read_b64_tr_b16): in each group of 16
+// lanes, lane i receives element (i % 4) of the 4-element words that lanes
+// i/4, 4 + i/4, 8 + i/4, 12 + i/4 address.
+__device__ __forceinline__ u32x2 lds_read_tr(const uint16_t *p) {
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(p));
+    return __builtin_bit_cast(u32x2, r);
+}
+
+// s_waitcnt vmcnt(0) alone (expcnt and lgkmcnt left at their maxima): the
+// global->LDS copies this wavefront issued have landed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ---------------------------------------------------------------------------
-// 16-bit core: one 64-query tile of one (image, head)
+// 16-bit core: the query tiles g, g+G, ... of one (image, head)
 // ---------------------------------------------------------------------------
-template <typename T, typename Rows>
+template <typename T, bool kPos, typename Rows>
 __device__ __forceinline__ void attend16(const uint16_t *__restrict__ q,
                                          const uint16_t *__restrict__ k,
                                          const uint16_t *__restrict__ v,
-                                         uint16_t *__restrict__ o, const Rows &R, int L, int q0,
-                                         float c, uint16_t *sK, uint16_t *sV,
+                                         uint16_t *__restrict__ o, const Rows &R, int L, float c,
+                                         int g, int G, uint16_t *sK, uint16_t *sV,
                                          uint16_t *__restrict__ cls_dst) {
     typedef typename Mma<T>::v8 V8;
+    constexpr uint32_t kOneBits = Mma<T>::kOnePair;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
-    // B operand of S^T = K Q^T: query row `col` of this wavefront, dims
-    // 32*kk + 8*grp .. +7
-    const int qrow = q0 + wid * kQW + col;
-    u32x4 qf0 = zero4, qf1 = zero4;
-    if (qrow < L) {
-        const uint16_t *src = q + R.at(qrow);
-        qf0 = *(const u32x4 *)(src + 8 * grp);
-        qf1 = *(const u32x4 *)(src + 32 + 8 * grp);
-    }
-
-    // Staging roles: threads 0..127 stage V (keys 4*sr .. 4*sr+3, dims
-    // 8*sc .. +7, transposed on the way into LDS); threads 128..255 stage K
-    // (keys sr + 16*i, dims 8*sc .. +7, row copies).
-    const bool vrole = tid < 128;
-    const int sr = (tid & 127) >> 3;
-    const int sc = tid & 7;
-    const uint16_t *stage_src = vrole ? v : k;
-    u32x4 g0, g1, g2, g3;
-
-#define RATTN_LOAD_CHUNK(CH)                                                            \
+    // Staging: wavefront w copies rows 16w .. 16w+15 of the K and V chunk, 8
+    // rows (1 KB) per DMA instruction; lane l fills row l/8, slot l%8.  Keys
+    // past the sequence end are not fetched: their K rows are masked out of
+    // the scores, their V rows are zeroed so 0-probability keys add exactly 0.
+    const int srow = lane >> 3, sslot = lane & 7;
+#define RATTN_STAGE(CH, BUF)                                                            \
     {                                                                                   \
-        const int k0_ = (CH) * kKC;                                                     \
-        const int key0_ = k0_ + (vrole ? 4 * sr : sr);                                 \
-        const int step_ = vrole ? 1 : 16;                                               \
-        g0 = key0_ < L ? *(const u32x4 *)(stage_src + R.at(key0_) + 8 * sc) : zero4;   \
-        g1 = key0_ + step_ < L ? *(const u32x4 *)(stage_src + R.at(key0_ + step_) + 8 * sc) : zero4; \
-        g2 = key0_ + 2 * step_ < L ? *(const u32x4 *)(stage_src + R.at(key0_ + 2 * step_) + 8 * sc) : zero4; \
-        g3 = key0_ + 3 * step_ < L ? *(const u32x4 *)(stage_src + R.at(key0_ + 3 * step_) + 8 * sc) : zero4; \
-    }
-
-    // V^T column of key j inside a chunk: (j & ~31) + 8*((j>>2)&3) + 4*((j>>4)&1) + (j&3)
-    const int vcol = (4 * sr & ~31) + 8 * ((sr) & 3) + 4 * ((4 * sr >> 4) & 1);
-#define RATTN_STORE_CHUNK(BUF)                                                          \
-    {                                                                                   \
-        if (vrole) {                                                                    \
-            uint16_t *dstv_ = sV + (BUF) * (kD * 64);                                   \
-            _Pragma("unroll") for (int e = 0; e < 8; ++e) {                             \
-                const int sh_ = 16 * (e & 1);                                           \
-                const uint32_t x0_ = (g0[e >> 1] >> sh_) & 0xFFFFu;                     \
-                const uint32_t x1_ = (g1[e >> 1] >> sh_) & 0xFFFFu;                     \
-                const uint32_t x2_ = (g2[e >> 1] >> sh_) & 0xFFFFu;                     \
-                const uint32_t x3_ = (g3[e >> 1] >> sh_) & 0xFFFFu;                     \
-                const u32x2 w_ = {x0_ | (x1_ << 16), x2_ | (x3_ << 16)};                \
-                const int row_ = 8 * sc + e;                                            \
-                *(u32x2 *)(dstv_ + swz(row_, vcol >> 3) + (vcol & 7)) = w_;             \
+        _Pragma("unroll") for (int hb_ = 0; hb_ < 2; ++hb_) {                           \
+            const int row0_ = 16 * wid + 8 * hb_;                                       \
+            const int row_ = row0_ + srow;                                              \
+            const int key_ = (CH) * kKC + row_;                                         \
+            uint16_t *kdst_ = sK + (BUF) * (kKC * 64) + row0_ * 64;                     \
+            uint16_t *vdst_ = sV + (BUF) * (kKC * 64) + row0_ * 64;                     \
+            if (key_ < L) {                                                             \
+                const int64_t ro_ = R.at(key_);                                         \
+                __builtin_amdgcn_global_load_lds(k + ro_ + 8 * kpiece(row_, sslot),      \
+                                                 RATTN_LDS(kdst_), 16, 0, 0);           \
+                __builtin_amdgcn_global_load_lds(v + ro_ + 8 * vpiece(row_, sslot),      \
+                                                 RATTN_LDS(vdst_), 16, 0, 0);           \
+            } else {                                                                    \
+                *(u32x4 *)(vdst_ + 8 * lane) = zero4;                                   \
             }                                                                           \
-        } else {                                                                        \
-            uint16_t *dstk_ = sK + (BUF) * (kKC * 64);                                  \
-            *(u32x4 *)(dstk_ + swz(sr, sc)) = g0;                                       \
-            *(u32x4 *)(dstk_ + swz(sr + 16, sc)) = g1;                                  \
-            *(u32x4 *)(dstk_ + swz(sr + 32, sc)) = g2;                                  \
-            *(u32x4 *)(dstk_ + swz(sr + 48, sc)) = g3;                                  \
         }                                                                               \
     }
 
-    float m = -INFINITY, lsum = 0.f;
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0, acc3 = acc0;
+    // B operand of S^T = K Q^T for query tile TILE: row `col` of this
+    // wavefront's 16 rows, dims 32*kk + 8*grp .. +7
+#define RATTN_LOAD_Q(TILE, A, B)                                                        \
+    {                                                                                   \
+        const int qr_ = (TILE) * kQT + wid * kQW + col;                                 \
+        A = zero4;                                                                      \
+        B = zero4;                                                                      \
+        if (qr_ < L) {                                                                  \
+            const uint16_t *src_ = q + R.at(qr_);                                       \
+            A = *(const u32x4 *)(src_ + 8 * grp);                                       \
+            B = *(const u32x4 *)(src_ + 32 + 8 * grp);                                  \
+        }                                                                               \
+    }
 
+    // This workgroup owns query tiles g, g+G, g+2G, ... of the sequence (G
+    // workgroups share one (image, head)).  Tiles and key chunks are both 64
+    // wide, so there are nch of each.  The work is one pipeline of steps
+    // (tile, chunk): the copy of the following step's K/V chunk -- the next
+    // chunk, or chunk 0 of the next tile -- and the next tile's Q rows are in
+    // flight while the current step computes.  With at most two chunks the
+    // double buffer holds the whole sequence, so only the first tile stages.
     const int nch = (L + kKC - 1) / kKC;
-    RATTN_LOAD_CHUNK(0)
-    RATTN_STORE_CHUNK(0)
+    if (g >= nch) return;
+    const bool resident = nch <= 2;
+    int t = g, ch = 0, step = 0;
+    u32x4 qf0, qf1;
+    RATTN_LOAD_Q(t, qf0, qf1)
+    RATTN_STAGE(0, 0)
+    wait_vmem();
     __syncthreads();
 
-    for (int ch = 0; ch < nch; ++ch) {
-        const int buf = ch & 1;
-        const bool more = ch + 1 < nch;
-        if (more) RATTN_LOAD_CHUNK(ch + 1)
+    // all-ones A operand: its product with P^T gives P's row sums
+    const V8 ones = __builtin_bit_cast(V8, u32x4{kOneBits, kOneBits, kOneBits, kOneBits});
+    float m = -INFINITY;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0, acc3 = acc0, accl = acc0;
+    while (true) {
+        int nt = t, nc = ch + 1;
+        if (nc == nch) {
+            nt = t + G;
+            nc = 0;
+        }
+        const bool has_next = nt < nch;
+        const bool next_tile = has_next && nc == 0;
+        const bool load_next = resident ? step + 1 < nch : has_next;
+        if (load_next) RATTN_STAGE(nc, (step + 1) & 1)
+        u32x4 qn0 = zero4, qn1 = zero4;
+        if (next_tile) RATTN_LOAD_Q(nt, qn0, qn1)
+
+        const int buf = resident ? ch : (step & 1);
         const uint16_t *Ks = sK + buf * (kKC * 64);
-        const uint16_t *Vs = sV + buf * (kD * 64);
+        const uint16_t *Vs = sV + buf * (kKC * 64);
+        const int valid = L - ch * kKC;            // keys of this chunk inside the sequence
+        const int nblk = valid >= kKC ? 4 : (valid + 15) >> 4;
 
-        f32x4 s[4];
+        // A wavefront whose 16 query rows all lie past the sequence end has
+        // nothing to compute (it still stages and meets every barrier).
+        if (t * kQT + wid * kQW < L) {
+            f32x4 s[4];
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            const int row = 16 * blk + col;
-            const u32x4 a0 = *(const u32x4 *)(Ks + swz(row, grp));
-            const u32x4 a1 = *(const u32x4 *)(Ks + swz(row, 4 + grp));
-            f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            z = Mma<T>::run(__builtin_bit_cast(V8, a0), __builtin_bit_cast(V8, qf0), z);
-            s[blk] = Mma<T>::run(__builtin_bit_cast(V8, a1), __builtin_bit_cast(V8, qf1), z);
+            for (int blk = 0; blk < 4; ++blk) {
+                if (blk < nblk) {
+                    const int row = 16 * blk + col;
+                    const u32x4 a0 = *(const u32x4 *)(Ks + row * 64 + 8 * kpiece(row, grp));
+                    const u32x4 a1 = *(const u32x4 *)(Ks + row * 64 + 8 * kpiece(row, 4 + grp));
+                    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                    z = Mma<T>::run(__builtin_bit_cast(V8, a0), __builtin_bit_cast(V8, qf0), z);
+                    s[blk] = Mma<T>::run(__builtin_bit_cast(V8, a1), __builtin_bit_cast(V8, qf1), z);
+                } else {
+                    s[blk] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+                }
+            }
+            if constexpr (kPos) {
+                // scale > 0: the largest score is the largest raw dot product,
+                // so the running max is kept in raw units and each probability
+                // is one fused multiply-add and one exp2.
+                if (valid < kKC) {
+#pragma unroll
+                    for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (16 * blk + 4 * grp + i >= valid) s[blk][i] = -INFINITY;
+                }
+                float mx = s[0][0];
+#pragma unroll
+                for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[blk][i]);
+                mx = max_across_groups(mx);
+                const float mn = fmaxf(m, mx);
+                const float alpha = fast_exp2((m - mn) * c);
+                m = mn;
+                const float mc = mn * c;
+#pragma unroll
+                for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) s[blk][i] = fast_exp2(__builtin_fmaf(s[blk][i], c, -mc));
+                acc0 *= alpha;
+                acc1 *= alpha;
+                acc2 *= alpha;
+                acc3 *= alpha;
+                accl[0] *= alpha;
+            } else {
+                // scale <= 0 (degenerate but valid): scale first, then mask
+                float mx = -INFINITY;
+#pragma unroll
+                for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float x = s[blk][i] * c;
+                        if (16 * blk + 4 * grp + i >= valid) x = -INFINITY;
+                        s[blk][i] = x;
+                        mx = fmaxf(mx, x);
+                    }
+                mx = max_across_groups(mx);
+                const float mn = fmaxf(m, mx);
+                const float alpha = fast_exp2(m - mn);
+                m = mn;
+#pragma unroll
+                for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) s[blk][i] = fast_exp2(s[blk][i] - mn);
+                acc0 *= alpha;
+                acc1 *= alpha;
+                acc2 *= alpha;
+                acc3 *= alpha;
+                accl[0] *= alpha;
+            }
+
+            // O^T += V^T P^T.  Operand slot (lane group g, slot s) of the
+            // 32-key step ks is key 32*ks + 16*(s/4) + 4*g + s%4: the key whose
+            // score the lane already holds in slot s%4 of block 2*ks + s/4.
+            // The V^T operand is read transposed out of row-major V: lane r of
+            // group g addresses key 32*ks + 16*h + 4*g + r/4, dims 16*dt + 4*(r%4).
+            // The row sums of the rounded P come from the same B operand
+            // against an all-ones A operand.
+            const int vr = 4 * grp + (col >> 2);
+            const int vp = (col & 3) >> 1, vh = 4 * (col & 1);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                if (32 * ks < valid) {
+                    u32x4 pb;
+                    pb[0] = pack2<T>(s[2 * ks][0], s[2 * ks][1]);
+                    pb[1] = pack2<T>(s[2 * ks][2], s[2 * ks][3]);
+                    pb[2] = pack2<T>(s[2 * ks + 1][0], s[2 * ks + 1][1]);
+                    pb[3] = pack2<T>(s[2 * ks + 1][2], s[2 * ks + 1][3]);
+                    const V8 b = __builtin_bit_cast(V8, pb);
+                    const int r0 = 32 * ks + vr, r1 = r0 + 16;
+                    const uint16_t *v0 = Vs + r0 * 64 + vh;
+                    const uint16_t *v1 = Vs + r1 * 64 + vh;
+                    f32x4 *accs[4] = {&acc0, &acc1, &acc2, &acc3};
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt) {
+                        const u32x2 lo = lds_read_tr(v0 + 8 * vpiece(r0, 2 * dt + vp));
+                        const u32x2 hi = lds_read_tr(v1 + 8 * vpiece(r1, 2 * dt + vp));
+                        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+                        *accs[dt] = Mma<T>::run(__builtin_bit_cast(V8, a), b, *accs[dt]);
+                    }
+                    accl = Mma<T>::run(ones, b, accl);
+                }
+            }
         }
 
-        const int valid = L - ch * kKC;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float x = s[blk][i] * c;
-                if (16 * blk + 4 * grp + i >= valid) x = -INFINITY;
-                s[blk][i] = x;
-                mx = fmaxf(mx, x);
+        if (ch == nch - 1) {
+            // tile t done: normalise and store; start the next tile afresh
+            const float inv = 1.f / accl[0];
+            const int qrow = t * kQT + wid * kQW + col;
+            if (qrow < L) {
+                // lane holds o[qrow][16*dt + 4*grp + i], i = 0..3
+                const u32x2 w0 = {pack2<T>(acc0[0] * inv, acc0[1] * inv), pack2<T>(acc0[2] * inv, acc0[3] * inv)};
+                const u32x2 w1 = {pack2<T>(acc1[0] * inv, acc1[1] * inv), pack2<T>(acc1[2] * inv, acc1[3] * inv)};
+                const u32x2 w2 = {pack2<T>(acc2[0] * inv, acc2[1] * inv), pack2<T>(acc2[2] * inv, acc2[3] * inv)};
+                const u32x2 w3 = {pack2<T>(acc3[0] * inv, acc3[1] * inv), pack2<T>(acc3[2] * inv, acc3[3] * inv)};
+                if (o) {
+                    uint16_t *orow = o + R.at(qrow) + 4 * grp;
+                    *(u32x2 *)(orow) = w0;
+                    *(u32x2 *)(orow + 16) = w1;
+                    *(u32x2 *)(orow + 32) = w2;
+                    *(u32x2 *)(orow + 48) = w3;
+                }
+                if (cls_dst && qrow == 0) {
+                    uint16_t *crow = cls_dst + 4 * grp;
+                    *(u32x2 *)(crow) = w0;
+                    *(u32x2 *)(crow + 16) = w1;
+                    *(u32x2 *)(crow + 32) = w2;
+                    *(u32x2 *)(crow + 48) = w3;
+                }
             }
-        mx = max_across_groups(mx);
-        const float mn = fmaxf(m, mx);
-        const float alpha = fast_exp2(m - mn);
-        m = mn;
-        float ps = 0.f;
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p = fast_exp2(s[blk][i] - mn);
-                s[blk][i] = p;
-                ps += p;
-            }
-        lsum = lsum * alpha + ps;
-        acc0 *= alpha;
-        acc1 *= alpha;
-        acc2 *= alpha;
-        acc3 *= alpha;
-
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            u32x4 pb;
-            pb[0] = pack2<T>(s[2 * ks][0], s[2 * ks][1]);
-            pb[1] = pack2<T>(s[2 * ks][2], s[2 * ks][3]);
-            pb[2] = pack2<T>(s[2 * ks + 1][0], s[2 * ks + 1][1]);
-            pb[3] = pack2<T>(s[2 * ks + 1][2], s[2 * ks + 1][3]);
-            const V8 b = __builtin_bit_cast(V8, pb);
-            const int piece = 4 * ks + grp;
-            acc0 = Mma<T>::run(__builtin_bit_cast(V8, *(const u32x4 *)(Vs + swz(col, piece))), b, acc0);
-            acc1 = Mma<T>::run(__builtin_bit_cast(V8, *(const u32x4 *)(Vs + swz(16 + col, piece))), b, acc1);
-            acc2 = Mma<T>::run(__builtin_bit_cast(V8, *(const u32x4 *)(Vs + swz(32 + col, piece))), b, acc2);
-            acc3 = Mma<T>::run(__builtin_bit_cast(V8, *(const u32x4 *)(Vs + swz(48 + col, piece))), b, acc3);
+            m = -INFINITY;
+            acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
+            acc1 = acc0;
+            acc2 = acc0;
+            acc3 = acc0;
+            accl = acc0;
         }
-        if (more) RATTN_STORE_CHUNK(buf ^ 1)
+        if (load_next) wait_vmem();
         __syncthreads();
-    }
-#undef RATTN_LOAD_CHUNK
-#undef RATTN_STORE_CHUNK
-
-    lsum = sum_across_groups(lsum);
-    const float inv = 1.f / lsum;
-    if (qrow < L) {
-        // lane holds o[qrow][16*dt + 4*grp + i], i = 0..3
-        const u32x2 w0 = {pack2<T>(acc0[0] * inv, acc0[1] * inv), pack2<T>(acc0[2] * inv, acc0[3] * inv)};
-        const u32x2 w1 = {pack2<T>(acc1[0] * inv, acc1[1] * inv), pack2<T>(acc1[2] * inv, acc1[3] * inv)};
-        const u32x2 w2 = {pack2<T>(acc2[0] * inv, acc2[1] * inv), pack2<T>(acc2[2] * inv, acc2[3] * inv)};
-        const u32x2 w3 = {pack2<T>(acc3[0] * inv, acc3[1] * inv), pack2<T>(acc3[2] * inv, acc3[3] * inv)};
-        if (o) {
-            uint16_t *orow = o + R.at(qrow) + 4 * grp;
-            *(u32x2 *)(orow) = w0;
-            *(u32x2 *)(orow + 16) = w1;
-            *(u32x2 *)(orow + 32) = w2;
-            *(u32x2 *)(orow + 48) = w3;
+        if (!has_next) break;
+        if (next_tile) {
+            qf0 = qn0;
+            qf1 = qn1;
         }
-        if (cls_dst && qrow == 0) {
-            uint16_t *crow = cls_dst + 4 * grp;
-            *(u32x2 *)(crow) = w0;
-            *(u32x2 *)(crow + 16) = w1;
-            *(u32x2 *)(crow + 32) = w2;
-            *(u32x2 *)(crow + 48) = w3;
-        }
+        t = nt;
+        ch = nc;
+        ++step;
     }
+#undef RATTN_LOAD_Q
+#undef RATTN_STAGE
 }
 
 // ---------------------------------------------------------------------------
-// float32 core
+// float32 core: all 64-query tiles of one (image, head), 32-key chunks
 // ---------------------------------------------------------------------------
 template <typename Rows>
 __device__ __forceinline__ void attend32(const float *__restrict__ q, const float *__restrict__ k,
                                          const float *__restrict__ v, float *__restrict__ o,
-                                         const Rows &R, int L, int q0, float c, float *sK,
-                                         float *sV, float *__restrict__ cls_dst) {
+                                         const Rows &R, int L, float c, float *sK, float *sV,
+                                         float *__restrict__ cls_dst) {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
-
-    // B operand of score step kk: Q[query col][4*kk + grp]
-    const int qrow = q0 + wid * kQW + col;
-    float qf[16];
-    {
-        const float *src = q + (qrow < L ? R.at(qrow) : R.at(0));
-#pragma unroll
-        for (int kk = 0; kk < 16; ++kk) qf[kk] = qrow < L ? src[4 * kk + grp] : 0.f;
-    }
 
     // staging: a chunk is 32 keys x 16 four-float vectors per tensor; thread
     // t stages vectors t and t + 256 of K and of V
@@ -345,206 +429,278 @@ __device__ __forceinline__ void attend32(const float *__restrict__ q, const floa
         *(u32x4 *)(dv_ + key_b * kLd32 + 4 * c4) = vb;                                 \
     }
 
-    float m = -INFINITY, lsum = 0.f;
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0, acc3 = acc0;
     const int nch = (L + kKC32 - 1) / kKC32;
-    RATTN_LOAD32(0)
-    RATTN_STORE32(0)
-    __syncthreads();
-    for (int ch = 0; ch < nch; ++ch) {
-        const int buf = ch & 1;
-        const bool more = ch + 1 < nch;
-        if (more) RATTN_LOAD32(ch + 1)
-        const float *Ks = sK + buf * (kKC32 * kLd32);
-        const float *Vs = sV + buf * (kKC32 * kLd32);
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+    const int ntile = (L + kQT - 1) / kQT;
+    const bool resident = nch <= 2;
+    for (int t = 0; t < ntile; ++t) {
+        // B operand of score step kk: Q[query col][4*kk + grp]
+        const int qrow = t * kQT + wid * kQW + col;
+        float qf[16];
+        {
+            const float *src = q + (qrow < L ? R.at(qrow) : R.at(0));
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-            s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[col * kLd32 + 4 * kk + grp], qf[kk], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[(16 + col) * kLd32 + 4 * kk + grp], qf[kk], s1, 0, 0, 0);
+            for (int kk = 0; kk < 16; ++kk) qf[kk] = qrow < L ? src[4 * kk + grp] : 0.f;
         }
-        const int valid = L - ch * kKC32;
-        float mx = -INFINITY;
+        const bool stage = !resident || t == 0;
+        if (stage) {
+            RATTN_LOAD32(0)
+            RATTN_STORE32(0)
+            __syncthreads();
+        }
+        float m = -INFINITY, lsum = 0.f;
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0, acc3 = acc0;
+        for (int ch = 0; ch < nch; ++ch) {
+            const int buf = ch & 1;
+            const bool more = stage && ch + 1 < nch;
+            if (more) RATTN_LOAD32(ch + 1)
+            const float *Ks = sK + buf * (kKC32 * kLd32);
+            const float *Vs = sV + buf * (kKC32 * kLd32);
+            f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float x0 = s0[i] * c, x1 = s1[i] * c;
-            if (4 * grp + i >= valid) x0 = -INFINITY;
-            if (16 + 4 * grp + i >= valid) x1 = -INFINITY;
-            s0[i] = x0;
-            s1[i] = x1;
-            mx = fmaxf(mx, fmaxf(x0, x1));
-        }
-        mx = max_across_groups(mx);
-        const float mn = fmaxf(m, mx);
-        const float alpha = fast_exp2(m - mn);
-        m = mn;
-        float ps = 0.f;
+            for (int kk = 0; kk < 16; ++kk) {
+                s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[col * kLd32 + 4 * kk + grp], qf[kk], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[(16 + col) * kLd32 + 4 * kk + grp], qf[kk], s1, 0, 0, 0);
+            }
+            const int valid = L - ch * kKC32;
+            float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            s0[i] = fast_exp2(s0[i] - mn);
-            s1[i] = fast_exp2(s1[i] - mn);
-            ps += s0[i] + s1[i];
-        }
-        lsum = lsum * alpha + ps;
-        acc0 *= alpha;
-        acc1 *= alpha;
-        acc2 *= alpha;
-        acc3 *= alpha;
-        // O^T += V^T P^T, one key per 16x16x4 step: lane group g supplies key
-        // 16*blk + 4*g + i, which is exactly the score it holds in slot i
+            for (int i = 0; i < 4; ++i) {
+                float x0 = s0[i] * c, x1 = s1[i] * c;
+                if (4 * grp + i >= valid) x0 = -INFINITY;
+                if (16 + 4 * grp + i >= valid) x1 = -INFINITY;
+                s0[i] = x0;
+                s1[i] = x1;
+                mx = fmaxf(mx, fmaxf(x0, x1));
+            }
+            mx = max_across_groups(mx);
+            const float mn = fmaxf(m, mx);
+            const float alpha = fast_exp2(m - mn);
+            m = mn;
+            float ps = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float *v0 = Vs + (4 * grp + i) * kLd32 + col;
-            const float *v1 = Vs + (16 + 4 * grp + i) * kLd32 + col;
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(v0[0], s0[i], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(v0[16], s0[i], acc1, 0, 0, 0);
-            acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(v0[32], s0[i], acc2, 0, 0, 0);
-            acc3 = __builtin_amdgcn_mfma_f32_16x16x4f32(v0[48], s0[i], acc3, 0, 0, 0);
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(v1[0], s1[i], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(v1[16], s1[i], acc1, 0, 0, 0);
-            acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(v1[32], s1[i], acc2, 0, 0, 0);
-            acc3 = __builtin_amdgcn_mfma_f32_16x16x4f32(v1[48], s1[i], acc3, 0, 0, 0);
+            for (int i = 0; i < 4; ++i) {
+                s0[i] = fast_exp2(s0[i] - mn);
+                s1[i] = fast_exp2(s1[i] - mn);
+                ps += s0[i] + s1[i];
+            }
+            lsum = lsum * alpha + ps;
+            acc0 *= alpha;
+            acc1 *= alpha;
+            acc2 *= alpha;
+            acc3 *= alpha;
+            // O^T += V^T P^T, one key per 16x16x4 step: lane group g supplies key
+            // 16*blk + 4*g + i, which is exactly the score it holds in slot i
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float *v0 = Vs + (4 * grp + i) * kLd32 + col;
+                const float *v1 = Vs + (16 + 4 * grp + i) * kLd32 + col;
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(v0[0], s0[i], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(v0[16], s0[i], acc1, 0, 0, 0);
+                acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(v0[32], s0[i], acc2, 0, 0, 0);
+                acc3 = __builtin_amdgcn_mfma_f32_16x16x4f32(v0[48], s0[i], acc3, 0, 0, 0);
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(v1[0], s1[i], acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(v1[16], s1[i], acc1, 0, 0, 0);
+                acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(v1[32], s1[i], acc2, 0, 0, 0);
+                acc3 = __builtin_amdgcn_mfma_f32_16x16x4f32(v1[48], s1[i], acc3, 0, 0, 0);
+            }
+            if (more) RATTN_STORE32(buf ^ 1)
+            __syncthreads();
         }
-        if (more) RATTN_STORE32(buf ^ 1)
-        __syncthreads();
+        lsum = sum_across_groups(lsum);
+        const float inv = 1.f / lsum;
+        if (qrow < L) {
+            if (o) {
+                float *orow = o + R.at(qrow) + 4 * grp;
+                *(f32x4 *)(orow) = acc0 * inv;
+                *(f32x4 *)(orow + 16) = acc1 * inv;
+                *(f32x4 *)(orow + 32) = acc2 * inv;
+                *(f32x4 *)(orow + 48) = acc3 * inv;
+            }
+            if (cls_dst && qrow == 0) {
+                float *crow = cls_dst + 4 * grp;
+                *(f32x4 *)(crow) = acc0 * inv;
+                *(f32x4 *)(crow + 16) = acc1 * inv;
+                *(f32x4 *)(crow + 32) = acc2 * inv;
+                *(f32x4 *)(crow + 48) = acc3 * inv;
+            }
+        }
     }
 #undef RATTN_LOAD32
 #undef RATTN_STORE32
-    lsum = sum_across_groups(lsum);
-    const float inv = 1.f / lsum;
-    if (qrow < L) {
-        if (o) {
-            float *orow = o + R.at(qrow) + 4 * grp;
-            *(f32x4 *)(orow) = acc0 * inv;
-            *(f32x4 *)(orow + 16) = acc1 * inv;
-            *(f32x4 *)(orow + 32) = acc2 * inv;
-            *(f32x4 *)(orow + 48) = acc3 * inv;
-        }
-        if (cls_dst && qrow == 0) {
-            float *crow = cls_dst + 4 * grp;
-            *(f32x4 *)(crow) = acc0 * inv;
-            *(f32x4 *)(crow + 16) = acc1 * inv;
-            *(f32x4 *)(crow + 32) = acc2 * inv;
-            *(f32x4 *)(crow + 48) = acc3 * inv;
-        }
-    }
 }
 
+// (image, head) of a one-workgroup-per-head launch.
+__device__ __forceinline__ void decode_pair(int H, int *b, int *h) {
+    *b = blockIdx.x / H;
+    *h = blockIdx.x - *b * H;
+}
+
+// (image, head, tile group) of this workgroup; false if the id is padding.
+// Workgroup ids are dealt to the 8 XCDs round-robin; the G workgroups of one
+// (image, head) get ids on the same XCD so the head's K/V rows, which each of
+// them streams, are read into one L2.
+__device__ __forceinline__ bool decode_group(int BH, int H, int G, int *b, int *h, int *g) {
+    const int id = blockIdx.x;
+    const int xcd = id & 7, local = id >> 3;
+    const int pair = (local / G) * 8 + xcd;
+    *g = local - (local / G) * G;
+    if (pair >= BH) return false;
+    *b = pair / H;
+    *h = pair - *b * H;
+    return true;
+}
+
+// Enough workgroups to keep every CU busy: one per (image, head) when there
+// are many heads in the batch, else each head's query tiles are dealt to up
+// to G workgroups (tiles g, g+G, ...).
+constexpr int64_t kTargetWorkgroups = 3072;
+
+int tile_groups(int B, int H, int max_seqlen) {
+    const int ntiles = max_seqlen > 0 ? (max_seqlen + kQT - 1) / kQT : 1;
+    const int64_t pairs = (int64_t)B * H;
+    const int64_t G = (kTargetWorkgroups + pairs - 1) / pairs;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(G, ntiles));
+}
+
+int64_t grid_for(int B, int H, int G) { return 8 * (((int64_t)B * H + 7) / 8) * G; }
+
 // ---------------------------------------------------------------------------
-// kernels on the flat ragged buffer
+// kernels on the flat ragged buffer: one workgroup per (image, head)
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(kThreads) void attn_fwd16(const uint16_t *__restrict__ q,
-                                                       const uint16_t *__restrict__ k,
-                                                       const uint16_t *__restrict__ v,
-                                                       uint16_t *__restrict__ o,
-                                                       const int32_t *__restrict__ cu, int B,
-                                                       int H, int ntiles, float c) {
+__global__ __launch_bounds__(kThreads, 4) void attn_fwd16(const uint16_t *__restrict__ q,
+                                                          const uint16_t *__restrict__ k,
+                                                          const uint16_t *__restrict__ v,
+                                                          uint16_t *__restrict__ o,
+                                                          const int32_t *__restrict__ cu, int B,
+                                                          int H, int G, float c) {
     __shared__ __attribute__((aligned(16))) uint16_t sK[2 * kKC * 64];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2 * kD * 64];
-    int b, h, tile;
-    if (!decode_tile(B, H, ntiles, &b, &h, &tile)) return;
+    int b, h, g;
+    if (!decode_group(B * H, H, G, &b, &h, &g)) return;
     const int seq0 = cu[b];
     const int L = cu[b + 1] - seq0;
-    const int q0 = tile * kQT;
-    if (q0 >= L) return;
+    if (L <= 0) return;
     const int64_t rs = (int64_t)H * kD;
     const FlatRows R = {(int64_t)seq0 * rs + (int64_t)h * kD, rs};
-    attend16<T>(q, k, v, o, R, L, q0, c, sK, sV, nullptr);
+    if (c > 0.f) attend16<T, true>(q, k, v, o, R, L, c, g, G, sK, sV, nullptr);
+    else attend16<T, false>(q, k, v, o, R, L, c, g, G, sK, sV, nullptr);
 }
 
 __global__ __launch_bounds__(kThreads) void attn_fwd32(const float *__restrict__ q,
                                                        const float *__restrict__ k,
                                                        const float *__restrict__ v,
                                                        float *__restrict__ o,
-                                                       const int32_t *__restrict__ cu, int B,
-                                                       int H, int ntiles, float c) {
+                                                       const int32_t *__restrict__ cu, int H,
+                                                       float c) {
     __shared__ __attribute__((aligned(16))) float sK[2 * kKC32 * kLd32];
     __shared__ __attribute__((aligned(16))) float sV[2 * kKC32 * kLd32];
-    int b, h, tile;
-    if (!decode_tile(B, H, ntiles, &b, &h, &tile)) return;
+    int b, h;
+    decode_pair(H, &b, &h);
     const int seq0 = cu[b];
     const int L = cu[b + 1] - seq0;
-    const int q0 = tile * kQT;
-    if (q0 >= L) return;
+    if (L <= 0) return;
     const int64_t rs = (int64_t)H * kD;
     const FlatRows R = {(int64_t)seq0 * rs + (int64_t)h * kD, rs};
-    attend32(q, k, v, o, R, L, q0, c, sK, sV, nullptr);
+    attend32(q, k, v, o, R, L, c, sK, sV, nullptr);
 }
 
 // ---------------------------------------------------------------------------
-// fused kernels: padded in, padded out, one launch
+// fused kernels: padded in, padded out, one launch, one workgroup per
+// (image, head)
 // ---------------------------------------------------------------------------
-// Kept positions of image b, in order, into pos[]; returns the count.  Wave 0
-// walks the mask 64 positions at a time with one ballot each.
+constexpr int kMaxChunksPerWave = (kMaxFusedN + 64 * kWaves - 1) / (64 * kWaves);
+
+// Kept positions of image b, in order, into pos[]; returns the count.  Every
+// wavefront loads the mask bytes of its 64-position chunks (chunk c belongs to
+// wave c % 4) in one round trip and ballots them; the ballots go to LDS as a
+// keep bitmap, and after one exchange of per-chunk counts each wavefront
+// writes its kept positions at their ranks.
 __device__ __forceinline__ int rank_image(const uint8_t *__restrict__ keep_img, int N,
-                                          int16_t *pos, int *s_count) {
-    if (threadIdx.x < 64) {
-        const int lane = threadIdx.x;
-        int count = 0;
-        for (int n0 = 0; n0 < N; n0 += 64) {
-            const int n = n0 + lane;
-            const bool kept = n < N && keep_img[n] != 0;
-            const uint64_t m = __ballot(kept);
-            if (kept) pos[count + __popcll(m & ((1ull << lane) - 1ull))] = (int16_t)n;
-            count += __popcll(m);
-        }
-        if (lane == 0) *s_count = count;
+                                          int16_t *pos, uint64_t *keep_bits) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int nchunk = (N + 63) / 64;
+    bool kept[kMaxChunksPerWave];
+#pragma unroll
+    for (int i = 0; i < kMaxChunksPerWave; ++i) {
+        const int n = 64 * (wid + kWaves * i) + lane;
+        kept[i] = n < N && keep_img[n] != 0;
+    }
+    uint64_t m[kMaxChunksPerWave];
+#pragma unroll
+    for (int i = 0; i < kMaxChunksPerWave; ++i) {
+        m[i] = __ballot(kept[i]);
+        const int chunk = wid + kWaves * i;
+        if (lane == 0 && chunk < nchunk) keep_bits[chunk] = m[i];
     }
     __syncthreads();
-    return *s_count;
+    int total = 0;
+    for (int cidx = 0; cidx < nchunk; ++cidx) total += __popcll(keep_bits[cidx]);
+#pragma unroll
+    for (int i = 0; i < kMaxChunksPerWave; ++i) {
+        const int chunk = wid + kWaves * i;
+        if (chunk >= nchunk) break;
+        int before = 0;
+        for (int cidx = 0; cidx < chunk; ++cidx) before += __popcll(keep_bits[cidx]);
+        if (kept[i]) pos[before + __popcll(m[i] & ((1ull << lane) - 1ull))] = (int16_t)(64 * chunk + lane);
+    }
+    __syncthreads();
+    return total;
 }
 
 // Zero rows of head h at the pruned positions of image b (and the CLS row
-// when position 0 was pruned); every thread writes 16-byte pieces.
+// when position 0 was pruned), reading the keep bitmap from LDS; every
+// thread writes 16-byte pieces, 8 or 16 threads per 128/256-byte row.
 template <int kPiecesPerRow>
-__device__ __forceinline__ void zero_pruned(const uint8_t *__restrict__ keep_img, int N,
+__device__ __forceinline__ void zero_pruned(const uint64_t *keep_bits, int N,
                                             u32x4 *__restrict__ out_head0, int64_t row_vec,
                                             u32x4 *__restrict__ cls_head) {
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
     if (out_head0) {
         for (int idx = threadIdx.x; idx < N * kPiecesPerRow; idx += kThreads) {
             const int n = idx / kPiecesPerRow, p = idx - n * kPiecesPerRow;
-            if (keep_img[n] == 0) out_head0[(int64_t)n * row_vec + p] = zero4;
+            if (!((keep_bits[n >> 6] >> (n & 63)) & 1ull)) out_head0[(int64_t)n * row_vec + p] = zero4;
         }
     }
-    if (cls_head && keep_img[0] == 0 && threadIdx.x < kPiecesPerRow) cls_head[threadIdx.x] = zero4;
+    if (cls_head && !(keep_bits[0] & 1ull) && threadIdx.x < kPiecesPerRow) cls_head[threadIdx.x] = zero4;
 }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void fused16(const uint16_t *__restrict__ q,
-                                                    const uint16_t *__restrict__ k,
-                                                    const uint16_t *__restrict__ v,
-                                                    const uint8_t *__restrict__ keep,
-                                                    uint16_t *__restrict__ out,
-                                                    uint16_t *__restrict__ cls, int B, int N,
-                                                    int H, int ntiles, float c) {
+__global__ __launch_bounds__(kThreads, 4) void fused16(const uint16_t *__restrict__ q,
+                                                       const uint16_t *__restrict__ k,
+                                                       const uint16_t *__restrict__ v,
+                                                       const uint8_t *__restrict__ keep,
+                                                       uint16_t *__restrict__ out,
+                                                       uint16_t *__restrict__ cls, int B, int N,
+                                                       int H, int G, float c) {
     __shared__ __attribute__((aligned(16))) uint16_t sK[2 * kKC * 64];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2 * kD * 64];
     __shared__ int16_t pos[kMaxFusedN];
-    __shared__ int s_count;
-    int b, h, tile;
-    if (!decode_tile(B, H, ntiles, &b, &h, &tile)) return;
+    __shared__ uint64_t keep_bits[kMaxFusedN / 64];
+    int b, h, g;
+    if (!decode_group(B * H, H, G, &b, &h, &g)) return;
     const uint8_t *keep_img = keep + (int64_t)b * N;
-    const int L = rank_image(keep_img, N, pos, &s_count);
+    const int L = rank_image(keep_img, N, pos, keep_bits);
     const int64_t rs = (int64_t)H * kD;
     const int64_t head0 = (int64_t)b * N * rs + (int64_t)h * kD;  // (b, 0, h)
     uint16_t *cls_head = cls ? cls + ((int64_t)b * H + h) * kD : nullptr;
-    if (tile == 0)
-        zero_pruned<kD * 2 / 16>(keep_img, N, out ? (u32x4 *)(out + head0) : nullptr, rs * 2 / 16,
-                                 (u32x4 *)cls_head);
-    const int q0 = tile * kQT;
-    if (q0 >= L) return;
+    if (g == 0)
+        zero_pruned<kD * 2 / 16>(keep_bits, N, out ? (u32x4 *)(out + head0) : nullptr,
+                                 rs * 2 / 16, (u32x4 *)cls_head);
+    if (L <= 0) return;
     const PaddedRows R = {head0, rs, pos};
     // the output row of query rank 0 is the CLS row iff position 0 was kept
     uint16_t *cls_dst = (cls_head && pos[0] == 0) ? cls_head : nullptr;
-    if (out) {
-        attend16<T>(q, k, v, out, R, L, q0, c, sK, sV, cls_dst);
-    } else {
-        // CLS rows only: only the tile holding rank 0 has work
-        if (tile != 0 || !cls_dst) return;
-        attend16<T>(q, k, v, nullptr, R, L, q0, c, sK, sV, cls_dst);
+    if (!out) {
+        // CLS rows only: only the workgroup holding query tile 0 has work
+        if (!cls_dst || g != 0) return;
+        const int one_tile = (L + kQT - 1) / kQT;
+        if (c > 0.f) attend16<T, true>(q, k, v, nullptr, R, L, c, 0, one_tile, sK, sV, cls_dst);
+        else attend16<T, false>(q, k, v, nullptr, R, L, c, 0, one_tile, sK, sV, cls_dst);
+        return;
     }
+    if (c > 0.f) attend16<T, true>(q, k, v, out, R, L, c, g, G, sK, sV, cls_dst);
+    else attend16<T, false>(q, k, v, out, R, L, c, g, G, sK, sV, cls_dst);
 }
 
 __global__ __launch_bounds__(kThreads) void fused32(const float *__restrict__ q,
@@ -552,85 +708,74 @@ __global__ __launch_bounds__(kThreads) void fused32(const float *__restrict__ q,
                                                     const float *__restrict__ v,
                                                     const uint8_t *__restrict__ keep,
                                                     float *__restrict__ out,
-                                                    float *__restrict__ cls, int B, int N, int H,
-                                                    int ntiles, float c) {
+                                                    float *__restrict__ cls, int N, int H,
+                                                    float c) {
     __shared__ __attribute__((aligned(16))) float sK[2 * kKC32 * kLd32];
     __shared__ __attribute__((aligned(16))) float sV[2 * kKC32 * kLd32];
     __shared__ int16_t pos[kMaxFusedN];
-    __shared__ int s_count;
-    int b, h, tile;
-    if (!decode_tile(B, H, ntiles, &b, &h, &tile)) return;
+    __shared__ uint64_t keep_bits[kMaxFusedN / 64];
+    int b, h;
+    decode_pair(H, &b, &h);
     const uint8_t *keep_img = keep + (int64_t)b * N;
-    const int L = rank_image(keep_img, N, pos, &s_count);
+    const int L = rank_image(keep_img, N, pos, keep_bits);
     const int64_t rs = (int64_t)H * kD;
     const int64_t head0 = (int64_t)b * N * rs + (int64_t)h * kD;
     float *cls_head = cls ? cls + ((int64_t)b * H + h) * kD : nullptr;
-    if (tile == 0)
-        zero_pruned<kD * 4 / 16>(keep_img, N, out ? (u32x4 *)(out + head0) : nullptr, rs * 4 / 16,
-                                 (u32x4 *)cls_head);
-    const int q0 = tile * kQT;
-    if (q0 >= L) return;
+    zero_pruned<kD * 4 / 16>(keep_bits, N, out ? (u32x4 *)(out + head0) : nullptr, rs * 4 / 16,
+                             (u32x4 *)cls_head);
+    if (L <= 0) return;
     const PaddedRows R = {head0, rs, pos};
     float *cls_dst = (cls_head && pos[0] == 0) ? cls_head : nullptr;
-    if (out) {
-        attend32(q, k, v, out, R, L, q0, c, sK, sV, cls_dst);
-    } else {
-        if (tile != 0 || !cls_dst) return;
-        attend32(q, k, v, nullptr, R, L, q0, c, sK, sV, cls_dst);
-    }
-}
-
-int64_t grid_for(int B, int H, int ntiles) {
-    const int64_t pairs = (int64_t)B * H;
-    return 8 * ((pairs + 7) / 8) * ntiles;
+    if (!out && !cls_dst) return;
+    attend32(q, k, v, out, R, L, c, sK, sV, cls_dst);
 }
 
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s) {
-    const int ntiles = (a.max_seqlen + kQT - 1) / kQT;
-    const unsigned grid = (unsigned)grid_for(a.B, a.H, ntiles);
     const float c = a.scale * kLog2e;
+    const int G = tile_groups(a.B, a.H, a.max_seqlen);
+    const unsigned grid = (unsigned)grid_for(a.B, a.H, G);
     switch (a.dt) {
     case Elem::BF16:
         hipLaunchKernelGGL(attn_fwd16<__bf16>, dim3(grid), dim3(kThreads), 0, s,
                            (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
-                           (uint16_t *)a.o, a.cu, a.B, a.H, ntiles, c);
+                           (uint16_t *)a.o, a.cu, a.B, a.H, G, c);
         break;
     case Elem::F16:
         hipLaunchKernelGGL(attn_fwd16<_Float16>, dim3(grid), dim3(kThreads), 0, s,
                            (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
-                           (uint16_t *)a.o, a.cu, a.B, a.H, ntiles, c);
+                           (uint16_t *)a.o, a.cu, a.B, a.H, G, c);
         break;
     case Elem::F32:
-        hipLaunchKernelGGL(attn_fwd32, dim3(grid), dim3(kThreads), 0, s, (const float *)a.q,
-                           (const float *)a.k, (const float *)a.v, (float *)a.o, a.cu, a.B, a.H,
-                           ntiles, c);
+        hipLaunchKernelGGL(attn_fwd32, dim3((unsigned)((int64_t)a.B * a.H)), dim3(kThreads), 0, s,
+                           (const float *)a.q, (const float *)a.k, (const float *)a.v,
+                           (float *)a.o, a.cu, a.H, c);
         break;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_fused(const FusedArgs &a, hipStream_t s) {
-    const int ntiles = (a.max_seqlen + kQT - 1) / kQT;
-    const unsigned grid = (unsigned)grid_for(a.B, a.H, ntiles > 0 ? ntiles : 1);
-    const int nt = ntiles > 0 ? ntiles : 1;
     const float c = a.scale * kLog2e;
+    // without the padded output only tile 0 (the CLS row) is computed
+    const int G = a.out ? tile_groups(a.B, a.H, std::min(a.max_seqlen, a.N)) : 1;
+    const unsigned grid = (unsigned)grid_for(a.B, a.H, G);
     switch (a.dt) {
     case Elem::BF16:
         hipLaunchKernelGGL(fused16<__bf16>, dim3(grid), dim3(kThreads), 0, s,
                            (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
-                           a.keep, (uint16_t *)a.out, (uint16_t *)a.cls, a.B, a.N, a.H, nt, c);
+                           a.keep, (uint16_t *)a.out, (uint16_t *)a.cls, a.B, a.N, a.H, G, c);
         break;
     case Elem::F16:
         hipLaunchKernelGGL(fused16<_Float16>, dim3(grid), dim3(kThreads), 0, s,
                            (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
-                           a.keep, (uint16_t *)a.out, (uint16_t *)a.cls, a.B, a.N, a.H, nt, c);
+                           a.keep, (uint16_t *)a.out, (uint16_t *)a.cls, a.B, a.N, a.H, G, c);
         break;
     case Elem::F32:
-        hipLaunchKernelGGL(fused32, dim3(grid), dim3(kThreads), 0, s, (const float *)a.q,
-                           (const float *)a.k, (const float *)a.v, a.keep, (float *)a.out,
-                           (float *)a.cls, a.B, a.N, a.H, nt, c);
+        hipLaunchKernelGGL(fused32, dim3((unsigned)((int64_t)a.B * a.H)), dim3(kThreads), 0, s,
+                           (const float *)a.q, (const float *)a.k, (const float *)a.v, a.keep,
+                           (float *)a.out, (float *)a.cls, a.N, a.H, c);
         break;
     }
     return hipGetLastError();
