@@ -1,0 +1,186 @@
+"""Run the rattn C ABI, built for x86 with the emulation shim, on CPU tensors and
+check every entry point against the oracle (test infrastructure).
+
+Usage: python run_cases.py LIBRARY CASE [CASE ...]
+
+The library is api.hip + pack.hip + attention.hip compiled by clang++ with
+tests/emu/hip/hip_runtime.h in place of HIP and AddressSanitizer on, so the
+kernels' own source runs lane by lane on the host and every out-of-bounds access
+aborts the process.  The binding is pointed at that library and told to accept
+host tensors; everything else (argument checks, launch geometry, kernels) is
+the product's code.  Exit status 0 means every case passed.
+"""
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import oracle  # noqa: E402
+import workloads  # noqa: E402
+from ragged_variable_length_amd import _binding  # noqa: E402
+import ragged_variable_length_amd as rv  # noqa: E402
+from tests import _gpu_util as U  # noqa: E402
+
+POISON = 0xA5
+
+
+def _host(t, name):
+    assert isinstance(t, torch.Tensor) and t.is_contiguous(), name
+    return t.data_ptr()
+
+
+def three_call(w, max_seqlen=None):
+    pipe = rv.RaggedPipeline(w.B, w.N, w.H, w.q.dtype, device="cpu")
+    for t in (pipe.pq, pipe.pk, pipe.pv, pipe.po):
+        t.view(torch.uint8).fill_(U.CANARY)
+    pipe.cu.fill_(-7)
+    pipe.run(w.q, w.k, w.v, w.keep, w.scale, max_seqlen=max_seqlen)
+    return {"cu": pipe.cu.numpy(), "max_seqlen": int(pipe.max_seqlen_dev.item()),
+            "total": int(pipe.total_dev.item()), "pq": pipe.pq, "pk": pipe.pk, "pv": pipe.pv,
+            "po": pipe.po, "out": pipe.out, "cls": pipe.cls}
+
+
+def fused(w, max_seqlen=None, want_out=True):
+    out = torch.empty_like(w.q)
+    cls = torch.empty((w.B, w.H, w.D), dtype=w.q.dtype)
+    for t in (out, cls):
+        t.view(torch.uint8).fill_(POISON)
+    rv.rattn_fused(w.q, w.k, w.v, w.keep, w.scale, out_padded=out if want_out else None,
+                   cls=cls, max_seqlen=max_seqlen)
+    return out, cls
+
+
+def check_both(w, flat=True, max_seqlen=None):
+    """3-call path: indexing bit-exact, attention within tolerance; fused path:
+    bitwise equal to the 3-call path's padded output and CLS rows (both run the
+    same attention core), and CLS-only mode equal too."""
+    t0 = time.time()
+    ref = oracle.pipeline(w, want_absw=True)
+    got = three_call(w, max_seqlen)
+    U.check_indexing(w, got, ref)
+    err, ratio = U.attention_error(w, got, ref["o64"], ref["absw"])
+    if flat:
+        assert err <= U.FLAT_TOL[w.dtype], (w.name, err)
+    assert ratio <= 1.0, (w.name, ratio)
+    fo, fc = fused(w, max_seqlen)
+    assert np.array_equal(U.bits(fo), U.bits(got["out"])), (w.name, "fused out")
+    assert np.array_equal(U.bits(fc), U.bits(got["cls"])), (w.name, "fused cls")
+    _, fc2 = fused(w, max_seqlen, want_out=False)
+    assert np.array_equal(U.bits(fc2), U.bits(got["cls"])), (w.name, "fused cls-only")
+    print(f"{w.name}: T={ref['total']} max|err|={err:.3e} err/bound={ratio:.3f} "
+          f"fused==3-call ({time.time() - t0:.0f}s)", flush=True)
+
+
+def _keep_lengths(lengths, N, seed):
+    g = torch.Generator().manual_seed(seed)
+    keep = torch.zeros((len(lengths), N), dtype=torch.uint8)
+    for b, L in enumerate(lengths):
+        keep[b, torch.randperm(N, generator=g)[:L]] = 1
+    return keep
+
+
+def case_tiny():
+    check_both(workloads.custom(3, 70, 1, "f32", p_keep=0.6, seed=3, name="small_f32"))
+
+
+def case_ragged():
+    # empty image, length one, pruned CLS, tails around the 16- and 64-row tiles
+    keep = _keep_lengths([1, 0, 17, 65, 130], 130, seed=40)
+    keep[3, 0] = 0
+    for dt in ("bf16", "f16", "f32"):
+        check_both(workloads.custom(5, 130, 1, dt, keep=keep.clone(), seed=41,
+                                    name=f"ragged_{dt}"), flat=False)
+
+
+def case_bounds():
+    # exact bound and four times N give the same bits
+    w = workloads.custom(2, 197, 2, "bf16", p_keep=0.5, seed=42, name="bounds_2x197")
+    check_both(w, max_seqlen=max(w.kept_counts))
+    a = three_call(w, max_seqlen=4 * w.N)
+    b = three_call(w)
+    assert np.array_equal(U.bits(a["po"]), U.bits(b["po"])), "max_seqlen bound changed bits"
+    print("max_seqlen exact / N / 4N: same bits", flush=True)
+
+
+def case_scan_large():
+    # B*N above the single-launch limit: one-workgroup scan, then the gather;
+    # pack and unpack only (the attention core is covered by the other cases)
+    w = workloads.custom(170, 100, 1, "bf16", p_keep=0.6, seed=116, name="scan_170x100")
+    cu_ref, mx_ref, T = oracle.scan(w.keep)
+    dst = torch.full((w.B * w.N, w.H, w.D), 7.0, dtype=w.q.dtype)
+    cu = torch.full((w.B + 1,), -7, dtype=torch.int32)
+    mx, tot = torch.zeros(1, dtype=torch.int32), torch.zeros(1, dtype=torch.int32)
+    rv.rattn_pack([w.q], [dst], w.keep, cu, mx, tot)
+    assert cu.numpy().tolist() == cu_ref.tolist() and int(mx) == mx_ref and int(tot) == T
+    assert np.array_equal(U.bits(dst[:T]), U.bits(oracle.pack(w.q, w.keep))), "pack"
+    assert (U.bits(dst[T:]) == U.bits(torch.tensor(7.0, dtype=w.q.dtype))).all(), "rows past T"
+    out = torch.full_like(w.q, 7.0)
+    cls = torch.full((w.B, w.H, w.D), 7.0, dtype=w.q.dtype)
+    rv.rattn_unpack(dst[:T].contiguous(), w.keep, cu, dst_padded=out, cls=cls)
+    ref_out, ref_cls = oracle.unpack(dst[:T], w.keep, cu_ref)
+    assert np.array_equal(U.bits(out), U.bits(ref_out)) and np.array_equal(U.bits(cls), U.bits(ref_cls))
+    print(f"scan_170x100: T={T} scan, pack, unpack bit-exact", flush=True)
+
+
+def case_small_rows():
+    # several images per 16-byte mask word
+    check_both(workloads.custom(3, 5, 1, "bf16", p_keep=0.6, seed=21, name="small_3x5"),
+               flat=False)
+
+
+def case_everything_pruned():
+    w = workloads.custom(3, 50, 2, "bf16", keep=torch.zeros((3, 50), dtype=torch.uint8), seed=14,
+                         name="all_pruned")
+    got = three_call(w)
+    assert got["cu"].tolist() == [0, 0, 0, 0] and got["total"] == 0 and got["max_seqlen"] == 0
+    assert not U.bits(got["out"]).any() and not U.bits(got["cls"]).any()
+    fo, fc = fused(w)
+    assert not U.bits(fo).any() and not U.bits(fc).any()
+    print("all_pruned: zero outputs on both paths", flush=True)
+
+
+def case_pack_subsets():
+    w = workloads.custom(3, 197, 2, "bf16", p_keep=0.3, seed=43, name="subsets")
+    cu_ref, _, T = oracle.scan(w.keep)
+    for n in (1, 2):
+        srcs = (w.q, w.k)[:n]
+        dsts = [torch.full((w.B * w.N, w.H, w.D), 7.0, dtype=w.q.dtype) for _ in range(n)]
+        cu = torch.empty(w.B + 1, dtype=torch.int32)
+        rv.rattn_pack(srcs, dsts, w.keep, cu)
+        assert cu.numpy().tolist() == cu_ref.tolist()
+        for s, d in zip(srcs, dsts):
+            assert np.array_equal(U.bits(d[:T]), U.bits(oracle.pack(s, w.keep))), f"pack n={n}"
+    flat = w.v.reshape(-1, w.H, w.D)[:T].contiguous()
+    cu = torch.from_numpy(cu_ref)
+    dst_ref, cls_ref = oracle.unpack(flat, w.keep, cu_ref)
+    cls = torch.full((w.B, w.H, w.D), 7.0, dtype=flat.dtype)
+    rv.rattn_unpack(flat, w.keep, cu, cls=cls)
+    out = torch.full((w.B, w.N, w.H, w.D), 7.0, dtype=flat.dtype)
+    rv.rattn_unpack(flat, w.keep, cu, dst_padded=out)
+    assert np.array_equal(U.bits(cls), U.bits(cls_ref)), "unpack CLS only"
+    assert np.array_equal(U.bits(out), U.bits(dst_ref)), "unpack padded only"
+    print("pack of 1 and 2 tensors, unpack CLS-only and padded-only: bit-exact", flush=True)
+
+
+CASES = {name[5:]: fn for name, fn in globals().items() if name.startswith("case_")}
+
+
+def main(argv):
+    _binding.LIB_PATH = argv[1]
+    _binding._lib = None
+    _binding._dev = _host
+    _binding._stream = lambda s: 0
+    rv.rattn_init()
+    for name in argv[2:]:
+        print(f"[case] {name}", flush=True)
+        CASES[name]()
+    print("EMULATED CASES PASSED", flush=True)
+
+
+if __name__ == "__main__":
+    main(sys.argv)
