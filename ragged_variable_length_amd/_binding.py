@@ -1,10 +1,14 @@
-"""ctypes binding of librattn.so -- argument marshalling only.
+"""Python binding of librattn.so -- argument marshalling only.
 
 Every function has the name of the C entry point it calls and does no compute:
 it reads shapes, dtypes, device pointers and the current HIP stream off torch
-tensors and passes them through.  All work runs in the library's HIP kernels.
-There is no fallback: if librattn.so is missing, or the call fails, an
-exception is raised.
+tensors and passes them through the CPython extension `_rattn` (one
+METH_FASTCALL function per entry point, linked against librattn.so).  All work
+runs in the library's HIP kernels.  There is no fallback: if librattn.so or the
+extension is missing, or a call fails, an exception is raised.
+
+`load()` returns librattn.so itself through ctypes, with prototypes, for
+callers that want the raw C ABI.
 """
 from __future__ import annotations
 
@@ -19,6 +23,9 @@ LIB_PATH = os.path.join(_HERE, "librattn.so")
 RATTN_OK = 0
 _DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _lib = None
+_ext_mod = None
+_NOT_BUILT = ("is not built: run `python -c \"import __graft_entry__ as g; g.build()\"` "
+              "(or python ragged_variable_length_amd/build.py) first")
 
 
 class RattnError(RuntimeError):
@@ -28,14 +35,12 @@ class RattnError(RuntimeError):
 
 
 def load() -> ctypes.CDLL:
-    """Load librattn.so (torch is imported first so the HIP runtime is shared)."""
+    """librattn.so through ctypes, with the C prototypes set."""
     global _lib
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        raise RuntimeError(
-            f"{LIB_PATH} is not built: run `python -c \"import __graft_entry__ as g; g.build()\"` "
-            "(or python ragged_variable_length_amd/build.py) first")
+        raise RuntimeError(f"{LIB_PATH} {_NOT_BUILT}")
     lib = ctypes.CDLL(LIB_PATH)
     P, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.rattn_init.argtypes = []
@@ -56,13 +61,35 @@ def load() -> ctypes.CDLL:
     return lib
 
 
+def ext():
+    """The `_rattn` extension module the entry-point wrappers call."""
+    global _ext_mod
+    if _ext_mod is not None:
+        return _ext_mod
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} {_NOT_BUILT}")
+    try:
+        from . import _rattn
+    except ImportError as e:
+        raise RuntimeError(f"the _rattn extension {_NOT_BUILT} ({e})") from e
+    _ext_mod = _rattn
+    return _ext_mod
+
+
 def status_string(status: int) -> str:
-    return load().rattn_status_string(int(status)).decode()
+    return ext().status_string(int(status))
 
 
-def _stream(stream) -> int:
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream, t: torch.Tensor) -> int:
+    """HIP stream handle: `stream` if given, else torch's current stream on t's
+    device."""
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
+        if _raw_stream is not None:
+            return _raw_stream(t.get_device())
+        return torch.cuda.current_stream(t.device).cuda_stream
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
@@ -84,7 +111,7 @@ def _check(fn: str, status: int) -> None:
 
 
 def rattn_init() -> None:
-    _check("rattn_init", load().rattn_init())
+    _check("rattn_init", ext().init())
 
 
 def rattn_pack(srcs, dsts, keep: torch.Tensor, cu_seqlens: torch.Tensor,
@@ -104,12 +131,10 @@ def rattn_pack(srcs, dsts, keep: torch.Tensor, cu_seqlens: torch.Tensor,
     row_elems = 1
     for x in row:
         row_elems *= int(x)
-    n = len(srcs)
-    src_arr = (ctypes.c_void_p * n)(*[_dev(s, "src") for s in srcs])
-    dst_arr = (ctypes.c_void_p * n)(*[_dev(d, "dst") for d in dsts])
-    st = load().rattn_pack(src_arr, dst_arr, n, _dev(keep, "keep"), B, N, row_elems,
-                           _DTYPE_CODE[dt], _dev(cu_seqlens, "cu_seqlens"),
-                           _opt(max_seqlen, "max_seqlen"), _opt(total, "total"), _stream(stream))
+    st = ext().pack([_dev(s, "src") for s in srcs], [_dev(d, "dst") for d in dsts],
+                    _dev(keep, "keep"), B, N, row_elems, _DTYPE_CODE[dt],
+                    _dev(cu_seqlens, "cu_seqlens"), _opt(max_seqlen, "max_seqlen"),
+                    _opt(total, "total"), _stream(stream, keep))
     _check("rattn_pack", st)
 
 
@@ -123,9 +148,9 @@ def rattn_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
         raise ValueError("rattn_forward: dtype mismatch")
     _, H, D = q.shape
     B = cu_seqlens.shape[0] - 1
-    st = load().rattn_forward(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"),
-                              _dev(cu_seqlens, "cu_seqlens"), B, int(max_seqlen), H, D,
-                              float(scale), _DTYPE_CODE[q.dtype], _stream(stream))
+    st = ext().forward(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"),
+                       _dev(cu_seqlens, "cu_seqlens"), B, int(max_seqlen), H, D, float(scale),
+                       _DTYPE_CODE[q.dtype], _stream(stream, q))
     _check("rattn_forward", st)
 
 
@@ -145,10 +170,34 @@ def rattn_unpack(src: torch.Tensor, keep: torch.Tensor, cu_seqlens: torch.Tensor
         raise ValueError("rattn_unpack: dst_padded must be [B, N, *row]")
     if cls is not None and tuple(cls.shape) != (B,) + tuple(src.shape[1:]):
         raise ValueError("rattn_unpack: cls must be [B, *row]")
-    st = load().rattn_unpack(_dev(src, "src"), _opt(dst_padded, "dst_padded"), _opt(cls, "cls"),
-                             _dev(keep, "keep"), _dev(cu_seqlens, "cu_seqlens"), B, N, row_elems,
-                             _DTYPE_CODE[src.dtype], _stream(stream))
+    st = ext().unpack(_dev(src, "src"), _opt(dst_padded, "dst_padded"), _opt(cls, "cls"),
+                      _dev(keep, "keep"), _dev(cu_seqlens, "cu_seqlens"), B, N, row_elems,
+                      _DTYPE_CODE[src.dtype], _stream(stream, src))
     _check("rattn_unpack", st)
+
+
+def fused_args(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep: torch.Tensor,
+               scale: float, out_padded: torch.Tensor | None = None,
+               cls: torch.Tensor | None = None, max_seqlen: int | None = None,
+               stream=None) -> tuple:
+    """Checked, marshalled argument tuple of one rattn_fused call."""
+    qs = q.shape
+    if len(qs) != 4 or k.shape != qs or v.shape != qs:
+        raise ValueError("rattn_fused: q, k, v must share one [B, N, H, head_dim] shape")
+    dt = q.dtype
+    if k.dtype != dt or v.dtype != dt:
+        raise ValueError("rattn_fused: dtype mismatch")
+    B, N, H, D = qs
+    if tuple(keep.shape) != (B, N):
+        raise ValueError("rattn_fused: keep must be [B, N]")
+    if out_padded is not None and (out_padded.shape != qs or out_padded.dtype != dt):
+        raise ValueError("rattn_fused: out_padded must match q")
+    if cls is not None and (tuple(cls.shape) != (B, H, D) or cls.dtype != dt):
+        raise ValueError("rattn_fused: cls must be [B, H, head_dim] of q's dtype")
+    ms = N if max_seqlen is None else int(max_seqlen)
+    return (_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(keep, "keep"),
+            _opt(out_padded, "out_padded"), _opt(cls, "cls"), B, N, H, D, ms, float(scale),
+            _DTYPE_CODE[dt], _stream(stream, q))
 
 
 def rattn_fused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep: torch.Tensor,
@@ -157,19 +206,5 @@ def rattn_fused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep: torch.T
                 stream=None) -> None:
     """Pack, attend and unpack in one launch, padded [B, N, H, 64] in and out
     (C: rattn_fused)."""
-    if not (q.shape == k.shape == v.shape) or q.dim() != 4:
-        raise ValueError("rattn_fused: q, k, v must share one [B, N, H, head_dim] shape")
-    if not (q.dtype == k.dtype == v.dtype):
-        raise ValueError("rattn_fused: dtype mismatch")
-    B, N, H, D = q.shape
-    if tuple(keep.shape) != (B, N):
-        raise ValueError("rattn_fused: keep must be [B, N]")
-    if out_padded is not None and (out_padded.shape != q.shape or out_padded.dtype != q.dtype):
-        raise ValueError("rattn_fused: out_padded must match q")
-    if cls is not None and (tuple(cls.shape) != (B, H, D) or cls.dtype != q.dtype):
-        raise ValueError("rattn_fused: cls must be [B, H, head_dim] of q's dtype")
-    ms = N if max_seqlen is None else int(max_seqlen)
-    st = load().rattn_fused(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(keep, "keep"),
-                            _opt(out_padded, "out_padded"), _opt(cls, "cls"), B, N, H, D, ms,
-                            float(scale), _DTYPE_CODE[q.dtype], _stream(stream))
+    st = ext().fused(*fused_args(q, k, v, keep, scale, out_padded, cls, max_seqlen, stream))
     _check("rattn_fused", st)

@@ -5,6 +5,7 @@ import os
 import shutil
 import subprocess
 import sys
+import sysconfig
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -15,6 +16,9 @@ SOURCES = ["api.hip", "pack.hip", "attention.hip"]
 # host-side timing loops used by bench.py (links librattn.so; not product ABI)
 BENCH_LIB = os.path.join(HERE, "librattn_bench.so")
 BENCH_SOURCES = ["bench_host.hip"]
+# CPython extension the Python binding calls (argument marshalling, links librattn.so)
+EXT = os.path.join(HERE, "_rattn" + sysconfig.get_config_var("EXT_SUFFIX"))
+EXT_SOURCE = "pymod.c"
 
 # Device-code flags: gfx950 only; packed-fp32 instruction selection off (the
 # compiler would otherwise form v_pk_* float ops on its own).
@@ -30,11 +34,30 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile librattn.so and librattn_bench.so next to this file (always rebuilds)."""
+    """Compile librattn.so, librattn_bench.so and the _rattn extension next to
+    this file (always rebuilds)."""
     _compile(LIB, SOURCES, [], verbose, extra_flags)
     _compile(BENCH_LIB, BENCH_SOURCES, ["-L", HERE, "-lrattn", "-Wl,-rpath,$ORIGIN"],
              verbose, extra_flags)
+    _compile_ext(verbose)
     return LIB
+
+
+def _compile_ext(verbose: bool) -> None:
+    cc = os.environ.get("CC") or shutil.which("gcc") or shutil.which("cc")
+    if not cc:
+        raise RuntimeError("no C compiler found for the _rattn extension")
+    tmp = EXT + ".tmp"
+    cmd = [cc, "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra", "-Werror",
+           "-I", sysconfig.get_paths()["include"], "-I", INCLUDE,
+           "-o", tmp, os.path.join(CSRC, EXT_SOURCE), "-L", HERE, "-lrattn",
+           "-Wl,-rpath,$ORIGIN"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("building the _rattn extension failed:\n" + res.stdout + res.stderr)
+    os.replace(tmp, EXT)
 
 
 def _compile(out: str, sources, link_flags, verbose: bool, extra_flags) -> None:

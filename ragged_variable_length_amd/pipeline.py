@@ -1,4 +1,4 @@
-"""Device buffers for repeated pack -> attend -> unpack calls.
+"""Device buffers and prepared calls for repeated pack -> attend -> unpack.
 
 Pages on "Dispatch-Aware Ragged Attention for Pruned Vision Transformers"
 (arXiv 2604.15408), radpulse.milrad-way.com write-up, section on the
@@ -8,12 +8,20 @@ Buffers are sized from (B, N, H) once, with capacity B*N rows for the flat
 tensors, so no call needs the kept-token count on the host: there is no
 device-to-host copy and no allocation inside `run`.  Every step is one of the
 three C entry points; nothing here computes.
+
+`FusedPlan` is the serving form of rattn_fused: its arguments are checked and
+marshalled once, so each `run()` is one extension call and one launch.  The
+same write-up (sections on FlashAttention-2's dispatch ceiling and on the
+Triton kernel) puts most of a small call's cost in per-call validation and
+binding crossings rather than in the kernel; a plan removes them from the
+repeated path.
 """
 from __future__ import annotations
 
 import torch
 
-from ._binding import rattn_forward, rattn_pack, rattn_unpack
+from . import _binding
+from ._binding import RattnError, rattn_forward, rattn_pack, rattn_unpack
 
 
 class RaggedPipeline:
@@ -52,3 +60,26 @@ class RaggedPipeline:
         self.attend(scale, max_seqlen, stream)
         self.unpack(keep, stream)
         return self.out, self.cls
+
+
+class FusedPlan:
+    """rattn_fused on fixed buffers: checked once, launched by `run()`.
+
+    q, k, v: padded [B, N, H, 64] device tensors; keep: uint8 [B, N]; at least
+    one of out_padded ([B, N, H, 64]) and cls ([B, H, 64]).  The stream is
+    fixed when the plan is made (None = torch's current stream then).  The
+    plan holds references to the tensors; their contents may change between
+    runs, their storage may not.
+    """
+
+    def __init__(self, q, k, v, keep, scale: float, out_padded=None, cls=None,
+                 max_seqlen: int | None = None, stream=None):
+        self._args = _binding.fused_args(q, k, v, keep, scale, out_padded, cls, max_seqlen,
+                                         stream)
+        self._tensors = (q, k, v, keep, out_padded, cls)
+        self._fn = _binding.ext().fused
+
+    def run(self) -> None:
+        st = self._fn(*self._args)
+        if st != 0:
+            raise RattnError("rattn_fused", st)

@@ -34,6 +34,41 @@ def _host(t, name):
     return t.data_ptr()
 
 
+class CtypesBackend:
+    """The `_rattn` extension's functions, served by the emulated library
+    through ctypes (the real extension links the gfx950 librattn.so)."""
+
+    def __init__(self, path):
+        import ctypes
+        self.c = ctypes
+        _binding.LIB_PATH = path
+        _binding._lib = None
+        self.lib = _binding.load()
+
+    def init(self):
+        return self.lib.rattn_init()
+
+    def status_string(self, s):
+        return self.lib.rattn_status_string(s).decode()
+
+    def version(self):
+        return self.lib.rattn_version()
+
+    def pack(self, srcs, dsts, *rest):
+        n = len(srcs)
+        P = self.c.c_void_p * n
+        return self.lib.rattn_pack(P(*srcs), P(*dsts), n, *rest)
+
+    def forward(self, *a):
+        return self.lib.rattn_forward(*a)
+
+    def unpack(self, *a):
+        return self.lib.rattn_unpack(*a)
+
+    def fused(self, *a):
+        return self.lib.rattn_fused(*a)
+
+
 def three_call(w, max_seqlen=None):
     pipe = rv.RaggedPipeline(w.B, w.N, w.H, w.q.dtype, device="cpu")
     for t in (pipe.pq, pipe.pk, pipe.pv, pipe.po):
@@ -171,10 +206,9 @@ CASES = {name[5:]: fn for name, fn in globals().items() if name.startswith("case
 
 
 def main(argv):
-    _binding.LIB_PATH = argv[1]
-    _binding._lib = None
+    _binding._ext_mod = CtypesBackend(argv[1])
     _binding._dev = _host
-    _binding._stream = lambda s: 0
+    _binding._stream = lambda s, t: 0
     rv.rattn_init()
     for name in argv[2:]:
         print(f"[case] {name}", flush=True)

@@ -148,3 +148,30 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         _binding.load()
+
+
+def test_extension_wraps_every_entry_point(lib):
+    ext = _binding.ext()
+    for name in declared_functions():
+        assert hasattr(ext, name[len("rattn_"):]), name
+    assert ext.version() == lib.rattn_version()
+    assert ext.status_string(INVALID) == rv.status_string(INVALID)
+    # the same host-side checks as through ctypes, same codes
+    assert ext.forward(A, A, A, A, A, 2, 10, 2, 63, 0.125, BF16, None) == UNSUPPORTED
+    assert ext.forward(None, A, A, A, A, 2, 10, 2, 64, 0.125, BF16, None) == INVALID
+    assert ext.fused(A, A, A, A, None, None, 2, 10, 2, 64, 10, 0.125, BF16, None) == INVALID
+    assert ext.unpack(A, A, A, A, A, 2, 10, 5, F32, None) == INVALID
+    assert ext.pack([A], [A], A, 2, 10, 128, 7, A, None, None, None) == INVALID
+    with pytest.raises(ValueError):
+        ext.pack([A] * 4, [A] * 4, A, 2, 10, 128, BF16, A, None, None, None)
+    with pytest.raises(TypeError):
+        ext.fused(A, A, A)
+    with pytest.raises(OverflowError):
+        ext.forward(A, A, A, A, A, 2 ** 40, 10, 2, 64, 0.125, BF16, None)
+
+
+def test_extension_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_binding, "_ext_mod", None)
+    monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _binding.ext()
