@@ -72,6 +72,10 @@ typedef enum rattn_dtype {
 #define RATTN_MAX_TENSORS 3    /* rattn_pack copies up to q, k and v at once  */
 #define RATTN_MAX_TOKENS 2147483647 /* B*N and T must fit in int32            */
 #define RATTN_MAX_FUSED_N 2048 /* longest padded sequence rattn_fused accepts  */
+/* Largest span, in bytes, of one image's rows of one tensor (max_seqlen rows
+ * for rattn_forward, N rows for rattn_fused): row offsets inside an image are
+ * 32-bit in the kernels.  Larger configurations return RATTN_ERR_UNSUPPORTED. */
+#define RATTN_MAX_IMAGE_BYTES 2147483648LL
 
 /* Checks once that a gfx950 device is present.  Idempotent and thread-safe;
  * called implicitly by the entry points.  RATTN_ERR_NO_DEVICE otherwise. */
@@ -116,11 +120,14 @@ rattn_status rattn_pack(const void *const *src, void *const *dst, int n_tensors,
  * cache, no log-sum-exp output.
  *
  *   q, k, v     device, [>= T, H, head_dim] of `dt` (T = cu[B])
- *   o           device, [>= T, H, head_dim] of `dt` (output; rows >= T and
- *               nothing else are written)
+ *   o           device, [>= T, H, head_dim] of `dt` (output; only rows < T
+ *               are written)
  *   cu_seqlens  device, int32 [B+1]
  *   B           images (>= 0)
- *   max_seqlen  host upper bound on every kept count (>= 0; 0 = nothing to do)
+ *   max_seqlen  host upper bound on every kept count (>= 0; 0 = nothing to do;
+ *               max_seqlen * H * head_dim * element size must not exceed
+ *               RATTN_MAX_IMAGE_BYTES).  An image whose kept count exceeds it
+ *               breaks the contract; its output rows are left unwritten.
  *   H           heads (>= 1);  head_dim must be RATTN_HEAD_DIM
  *   scale       finite float multiplying the dot products (1/sqrt(64) for ViT)
  * Arithmetic: q.k and p.v contractions on the matrix cores with float32
@@ -165,7 +172,8 @@ rattn_status rattn_unpack(const void *src, void *dst_padded, void *cls,
  *               the attention output, pruned positions all-zero bytes
  *   cls         device, [B, H, head_dim] (nullable): row (b, 0) of that
  *               output (zeros when the CLS token was pruned)
- *   B, N, H     B >= 0, 1 <= N <= RATTN_MAX_FUSED_N, H >= 1
+ *   B, N, H     B >= 0, 1 <= N <= RATTN_MAX_FUSED_N, H >= 1, and
+ *               N * H * head_dim * element size <= RATTN_MAX_IMAGE_BYTES
  *   head_dim    must be RATTN_HEAD_DIM
  *   max_seqlen  host upper bound on every kept count (N is always valid)
  *   scale, dt   as for rattn_forward

@@ -116,6 +116,9 @@ rattn_status rattn_forward(const void *q, const void *k, const void *v, void *o,
     if (B < 0 || H < 1 || max_seqlen < 0 || !std::isfinite(scale)) return RATTN_ERR_INVALID_ARG;
     if (head_dim != RATTN_HEAD_DIM) return RATTN_ERR_UNSUPPORTED;
     if ((int64_t)H * head_dim > (1 << 24)) return RATTN_ERR_INVALID_ARG;
+    // row offsets inside one image are 32-bit in the kernels
+    if ((int64_t)max_seqlen * H * head_dim * elem_size(dt) > RATTN_MAX_IMAGE_BYTES)
+        return RATTN_ERR_UNSUPPORTED;
     if (B == 0 || max_seqlen == 0) return RATTN_OK;  // nothing to attend
     if (!q || !k || !v || !o || !cu_seqlens) return RATTN_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(cu_seqlens))
@@ -174,6 +177,7 @@ rattn_status rattn_fused(const void *q, const void *k, const void *v, const uint
     if ((int64_t)B * N > RATTN_MAX_TOKENS || (int64_t)H * RATTN_HEAD_DIM > (1 << 24))
         return RATTN_ERR_INVALID_ARG;
     if (head_dim != RATTN_HEAD_DIM || N > RATTN_MAX_FUSED_N) return RATTN_ERR_UNSUPPORTED;
+    if ((int64_t)N * H * head_dim * elem_size(dt) > RATTN_MAX_IMAGE_BYTES) return RATTN_ERR_UNSUPPORTED;
     if (!out_padded && !cls) return RATTN_ERR_INVALID_ARG;
     if (B == 0) return RATTN_OK;
     if (!q || !k || !v || !keep) return RATTN_ERR_INVALID_ARG;

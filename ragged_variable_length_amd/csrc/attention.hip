@@ -80,38 +80,50 @@ template <> struct Mma<_Float16> {
     }
 };
 
+// Lanes l, l^16, l^32 and l^48 hold the same query row: two lane swaps
+// (v_permlane32_swap, v_permlane16_swap) give every lane the maximum of the four.
 __device__ __forceinline__ float max_across_groups(float x) {
-    // lanes l, l^16, l^32, l^48 hold the same query row
-    x = fmaxf(x, __shfl_xor(x, 16));
-    x = fmaxf(x, __shfl_xor(x, 32));
-    return x;
+    uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    x = fmaxf(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
+    u = __builtin_bit_cast(uint32_t, x);
+    const auto b = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]));
 }
 
 __device__ __forceinline__ float sum_across_groups(float x) {
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
+    uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    x = __builtin_bit_cast(float, (uint32_t)a[0]) + __builtin_bit_cast(float, (uint32_t)a[1]);
+    u = __builtin_bit_cast(uint32_t, x);
+    const auto b = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (uint32_t)b[0]) + __builtin_bit_cast(float, (uint32_t)b[1]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats rounded to nearest even and packed (v_cvt_pk_bf16_f32 /
+// v_cvt_pk_f16_f32).
 template <typename T>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    T a = (T)lo, b = (T)hi;  // round to nearest even
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    typedef T T2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, T2));
 }
 
-// Element offset of the 64-element head slice of kept row r of one
-// (image, head), in the flat ragged buffer or in the padded tensor.
+// Element offset, from the (image, head) base, of the 64-element head slice
+// of kept row r: in the flat ragged buffer (rows consecutive) or in the padded
+// tensor (row at its original position).  32-bit: the host checks that one
+// image's rows span less than 2^31 bytes.
 struct FlatRows {
-    int64_t base, rs;  // offset of (cu[b], h); elements per token row
-    __device__ __forceinline__ int64_t at(int r) const { return base + (int64_t)r * rs; }
+    uint32_t rs;  // elements per token row
+    __device__ __forceinline__ uint32_t off(int r) const { return (uint32_t)r * rs; }
 };
 struct PaddedRows {
-    int64_t base, rs;    // offset of (b, 0, h); elements per token row
+    uint32_t rs;
     const int16_t *pos;  // LDS: position of the r-th kept token
-    __device__ __forceinline__ int64_t at(int r) const { return base + (int64_t)pos[r] * rs; }
+    __device__ __forceinline__ uint32_t off(int r) const { return (uint32_t)pos[r] * rs; }
 };
 
 // LDS tiles of the 16-bit path are 64 rows x 128 bytes, written by
@@ -144,15 +156,16 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // 16-bit core: the query tiles g, g+G, ... of one (image, head)
 // ---------------------------------------------------------------------------
 template <typename T, bool kPos, typename Rows>
-__device__ __forceinline__ void attend16(const uint16_t *__restrict__ q,
-                                         const uint16_t *__restrict__ k,
-                                         const uint16_t *__restrict__ v,
-                                         uint16_t *__restrict__ o, const Rows &R, int L, float c,
+__device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
+                                         const uint16_t *__restrict__ kh,
+                                         const uint16_t *__restrict__ vh,
+                                         uint16_t *__restrict__ oh, const Rows &R, int L, float c,
                                          int g, int G, uint16_t *sK, uint16_t *sV,
                                          uint16_t *__restrict__ cls_dst) {
     typedef typename Mma<T>::v8 V8;
     constexpr uint32_t kOneBits = Mma<T>::kOnePair;
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15, grp = lane >> 4;
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
@@ -161,39 +174,37 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ q,
     // past the sequence end are not fetched: their K rows are masked out of
     // the scores, their V rows are zeroed so 0-probability keys add exactly 0.
     const int srow = lane >> 3, sslot = lane & 7;
-#define RATTN_STAGE(CH, BUF)                                                            \
-    {                                                                                   \
-        _Pragma("unroll") for (int hb_ = 0; hb_ < 2; ++hb_) {                           \
-            const int row0_ = 16 * wid + 8 * hb_;                                       \
-            const int row_ = row0_ + srow;                                              \
-            const int key_ = (CH) * kKC + row_;                                         \
-            uint16_t *kdst_ = sK + (BUF) * (kKC * 64) + row0_ * 64;                     \
-            uint16_t *vdst_ = sV + (BUF) * (kKC * 64) + row0_ * 64;                     \
-            if (key_ < L) {                                                             \
-                const int64_t ro_ = R.at(key_);                                         \
-                __builtin_amdgcn_global_load_lds(k + ro_ + 8 * kpiece(row_, sslot),      \
-                                                 RATTN_LDS(kdst_), 16, 0, 0);           \
-                __builtin_amdgcn_global_load_lds(v + ro_ + 8 * vpiece(row_, sslot),      \
-                                                 RATTN_LDS(vdst_), 16, 0, 0);           \
-            } else {                                                                    \
-                *(u32x4 *)(vdst_ + 8 * lane) = zero4;                                   \
-            }                                                                           \
-        }                                                                               \
-    }
-
-    // B operand of S^T = K Q^T for query tile TILE: row `col` of this
-    // wavefront's 16 rows, dims 32*kk + 8*grp .. +7
-#define RATTN_LOAD_Q(TILE, A, B)                                                        \
-    {                                                                                   \
-        const int qr_ = (TILE) * kQT + wid * kQW + col;                                 \
-        A = zero4;                                                                      \
-        B = zero4;                                                                      \
-        if (qr_ < L) {                                                                  \
-            const uint16_t *src_ = q + R.at(qr_);                                       \
-            A = *(const u32x4 *)(src_ + 8 * grp);                                       \
-            B = *(const u32x4 *)(src_ + 32 + 8 * grp);                                  \
-        }                                                                               \
-    }
+    auto stage = [&](int chunk, int buf) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            const int row0 = 16 * wid + 8 * hb;
+            const int row = row0 + srow;
+            const int key = chunk * kKC + row;
+            uint16_t *kdst = sK + buf * (kKC * 64) + row0 * 64;
+            uint16_t *vdst = sV + buf * (kKC * 64) + row0 * 64;
+            if (key < L) {
+                const uint32_t ro = R.off(key);
+                __builtin_amdgcn_global_load_lds(kh + ro + 8 * kpiece(row, sslot), RATTN_LDS(kdst),
+                                                 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(vh + ro + 8 * vpiece(row, sslot), RATTN_LDS(vdst),
+                                                 16, 0, 0);
+            } else {
+                *(u32x4 *)(vdst + 8 * lane) = zero4;
+            }
+        }
+    };
+    // B operand of S^T = K Q^T for query tile `tile`: row `col` of this
+    // wavefront's 16 rows, dims 8*grp .. +7 and 32 + 8*grp .. +7
+    auto load_q = [&](int tile, u32x4 &a, u32x4 &b) {
+        const int qr = tile * kQT + wid * kQW + col;
+        a = zero4;
+        b = zero4;
+        if (qr < L) {
+            const uint16_t *src = qh + R.off(qr);
+            a = *(const u32x4 *)(src + 8 * grp);
+            b = *(const u32x4 *)(src + 32 + 8 * grp);
+        }
+    };
 
     // This workgroup owns query tiles g, g+G, g+2G, ... of the sequence (G
     // workgroups share one (image, head)).  Tiles and key chunks are both 64
@@ -206,14 +217,16 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ q,
     if (g >= nch) return;
     const bool resident = nch <= 2;
     int t = g, ch = 0, step = 0;
-    u32x4 qf0, qf1;
-    RATTN_LOAD_Q(t, qf0, qf1)
-    RATTN_STAGE(0, 0)
+    u32x4 qf0, qf1, qn0 = zero4, qn1 = zero4;
+    load_q(t, qf0, qf1);
+    stage(0, 0);
     wait_vmem();
     __syncthreads();
 
     // all-ones A operand: its product with P^T gives P's row sums
     const V8 ones = __builtin_bit_cast(V8, u32x4{kOneBits, kOneBits, kOneBits, kOneBits});
+    const int vr = 4 * grp + (col >> 2);
+    const int vp = (col & 3) >> 1, vhalf = 4 * (col & 1);
     float m = -INFINITY;
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0, acc3 = acc0, accl = acc0;
     while (true) {
@@ -225,32 +238,29 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ q,
         const bool has_next = nt < nch;
         const bool next_tile = has_next && nc == 0;
         const bool load_next = resident ? step + 1 < nch : has_next;
-        if (load_next) RATTN_STAGE(nc, (step + 1) & 1)
-        u32x4 qn0 = zero4, qn1 = zero4;
-        if (next_tile) RATTN_LOAD_Q(nt, qn0, qn1)
+        if (load_next) stage(nc, (step + 1) & 1);
+        if (next_tile) load_q(nt, qn0, qn1);
 
         const int buf = resident ? ch : (step & 1);
         const uint16_t *Ks = sK + buf * (kKC * 64);
         const uint16_t *Vs = sV + buf * (kKC * 64);
-        const int valid = L - ch * kKC;            // keys of this chunk inside the sequence
-        const int nblk = valid >= kKC ? 4 : (valid + 15) >> 4;
+        const int valid = L - ch * kKC;  // keys of this chunk inside the sequence
 
         // A wavefront whose 16 query rows all lie past the sequence end has
         // nothing to compute (it still stages and meets every barrier).
         if (t * kQT + wid * kQW < L) {
+            // S^T for the 64 keys of the chunk.  Every block is computed:
+            // rows of keys past the end hold stale LDS data whose scores are
+            // replaced by -inf below, so no branch sits between the reads.
             f32x4 s[4];
 #pragma unroll
             for (int blk = 0; blk < 4; ++blk) {
-                if (blk < nblk) {
-                    const int row = 16 * blk + col;
-                    const u32x4 a0 = *(const u32x4 *)(Ks + row * 64 + 8 * kpiece(row, grp));
-                    const u32x4 a1 = *(const u32x4 *)(Ks + row * 64 + 8 * kpiece(row, 4 + grp));
-                    f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                    z = Mma<T>::run(__builtin_bit_cast(V8, a0), __builtin_bit_cast(V8, qf0), z);
-                    s[blk] = Mma<T>::run(__builtin_bit_cast(V8, a1), __builtin_bit_cast(V8, qf1), z);
-                } else {
-                    s[blk] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-                }
+                const int row = 16 * blk + col;
+                const u32x4 a0 = *(const u32x4 *)(Ks + row * 64 + 8 * kpiece(row, grp));
+                const u32x4 a1 = *(const u32x4 *)(Ks + row * 64 + 8 * kpiece(row, 4 + grp));
+                f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                z = Mma<T>::run(__builtin_bit_cast(V8, a0), __builtin_bit_cast(V8, qf0), z);
+                s[blk] = Mma<T>::run(__builtin_bit_cast(V8, a1), __builtin_bit_cast(V8, qf1), z);
             }
             if constexpr (kPos) {
                 // scale > 0: the largest score is the largest raw dot product,
@@ -263,11 +273,10 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ q,
                         for (int i = 0; i < 4; ++i)
                             if (16 * blk + 4 * grp + i >= valid) s[blk][i] = -INFINITY;
                 }
-                float mx = s[0][0];
+                float mx = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
 #pragma unroll
-                for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[blk][i]);
+                for (int blk = 1; blk < 4; ++blk)
+                    mx = fmaxf(fmaxf(mx, fmaxf(s[blk][0], s[blk][1])), fmaxf(s[blk][2], s[blk][3]));
                 mx = max_across_groups(mx);
                 const float mn = fmaxf(m, mx);
                 const float alpha = fast_exp2((m - mn) * c);
@@ -284,16 +293,22 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ q,
                 accl[0] *= alpha;
             } else {
                 // scale <= 0 (degenerate but valid): scale first, then mask
+#pragma unroll
+                for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) s[blk][i] *= c;
+                if (valid < kKC) {
+#pragma unroll
+                    for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (16 * blk + 4 * grp + i >= valid) s[blk][i] = -INFINITY;
+                }
                 float mx = -INFINITY;
 #pragma unroll
                 for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float x = s[blk][i] * c;
-                        if (16 * blk + 4 * grp + i >= valid) x = -INFINITY;
-                        s[blk][i] = x;
-                        mx = fmaxf(mx, x);
-                    }
+                    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[blk][i]);
                 mx = max_across_groups(mx);
                 const float mn = fmaxf(m, mx);
                 const float alpha = fast_exp2(m - mn);
@@ -316,11 +331,9 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ q,
             // group g addresses key 32*ks + 16*h + 4*g + r/4, dims 16*dt + 4*(r%4).
             // The row sums of the rounded P come from the same B operand
             // against an all-ones A operand.
-            const int vr = 4 * grp + (col >> 2);
-            const int vp = (col & 3) >> 1, vh = 4 * (col & 1);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                if (32 * ks < valid) {
+                if (ks == 0 || valid > 32) {
                     u32x4 pb;
                     pb[0] = pack2<T>(s[2 * ks][0], s[2 * ks][1]);
                     pb[1] = pack2<T>(s[2 * ks][2], s[2 * ks][3]);
@@ -328,8 +341,8 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ q,
                     pb[3] = pack2<T>(s[2 * ks + 1][2], s[2 * ks + 1][3]);
                     const V8 b = __builtin_bit_cast(V8, pb);
                     const int r0 = 32 * ks + vr, r1 = r0 + 16;
-                    const uint16_t *v0 = Vs + r0 * 64 + vh;
-                    const uint16_t *v1 = Vs + r1 * 64 + vh;
+                    const uint16_t *v0 = Vs + r0 * 64 + vhalf;
+                    const uint16_t *v1 = Vs + r1 * 64 + vhalf;
                     f32x4 *accs[4] = {&acc0, &acc1, &acc2, &acc3};
 #pragma unroll
                     for (int dt = 0; dt < 4; ++dt) {
@@ -345,16 +358,16 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ q,
 
         if (ch == nch - 1) {
             // tile t done: normalise and store; start the next tile afresh
-            const float inv = 1.f / accl[0];
             const int qrow = t * kQT + wid * kQW + col;
             if (qrow < L) {
+                const float inv = __builtin_amdgcn_rcpf(accl[0]);
                 // lane holds o[qrow][16*dt + 4*grp + i], i = 0..3
                 const u32x2 w0 = {pack2<T>(acc0[0] * inv, acc0[1] * inv), pack2<T>(acc0[2] * inv, acc0[3] * inv)};
                 const u32x2 w1 = {pack2<T>(acc1[0] * inv, acc1[1] * inv), pack2<T>(acc1[2] * inv, acc1[3] * inv)};
                 const u32x2 w2 = {pack2<T>(acc2[0] * inv, acc2[1] * inv), pack2<T>(acc2[2] * inv, acc2[3] * inv)};
                 const u32x2 w3 = {pack2<T>(acc3[0] * inv, acc3[1] * inv), pack2<T>(acc3[2] * inv, acc3[3] * inv)};
-                if (o) {
-                    uint16_t *orow = o + R.at(qrow) + 4 * grp;
+                if (oh) {
+                    uint16_t *orow = oh + R.off(qrow) + 4 * grp;
                     *(u32x2 *)(orow) = w0;
                     *(u32x2 *)(orow + 16) = w1;
                     *(u32x2 *)(orow + 32) = w2;
@@ -386,8 +399,6 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ q,
         ch = nc;
         ++step;
     }
-#undef RATTN_LOAD_Q
-#undef RATTN_STAGE
 }
 
 // ---------------------------------------------------------------------------
@@ -411,12 +422,12 @@ __device__ __forceinline__ void attend32(const float *__restrict__ q, const floa
         const int k0_ = (CH) * kKC32;                                                  \
         ka = zero4; va = zero4; kb = zero4; vb = zero4;                                \
         if (k0_ + key_a < L) {                                                         \
-            ka = *(const u32x4 *)(k + R.at(k0_ + key_a) + 4 * c4);                     \
-            va = *(const u32x4 *)(v + R.at(k0_ + key_a) + 4 * c4);                     \
+            ka = *(const u32x4 *)(k + R.off(k0_ + key_a) + 4 * c4);                     \
+            va = *(const u32x4 *)(v + R.off(k0_ + key_a) + 4 * c4);                     \
         }                                                                              \
         if (k0_ + key_b < L) {                                                         \
-            kb = *(const u32x4 *)(k + R.at(k0_ + key_b) + 4 * c4);                     \
-            vb = *(const u32x4 *)(v + R.at(k0_ + key_b) + 4 * c4);                     \
+            kb = *(const u32x4 *)(k + R.off(k0_ + key_b) + 4 * c4);                     \
+            vb = *(const u32x4 *)(v + R.off(k0_ + key_b) + 4 * c4);                     \
         }                                                                              \
     }
 #define RATTN_STORE32(BUF)                                                             \
@@ -437,7 +448,7 @@ __device__ __forceinline__ void attend32(const float *__restrict__ q, const floa
         const int qrow = t * kQT + wid * kQW + col;
         float qf[16];
         {
-            const float *src = q + (qrow < L ? R.at(qrow) : R.at(0));
+            const float *src = q + (qrow < L ? R.off(qrow) : 0u);
 #pragma unroll
             for (int kk = 0; kk < 16; ++kk) qf[kk] = qrow < L ? src[4 * kk + grp] : 0.f;
         }
@@ -510,7 +521,7 @@ __device__ __forceinline__ void attend32(const float *__restrict__ q, const floa
         const float inv = 1.f / lsum;
         if (qrow < L) {
             if (o) {
-                float *orow = o + R.at(qrow) + 4 * grp;
+                float *orow = o + R.off(qrow) + 4 * grp;
                 *(f32x4 *)(orow) = acc0 * inv;
                 *(f32x4 *)(orow + 16) = acc1 * inv;
                 *(f32x4 *)(orow + 32) = acc2 * inv;
@@ -550,15 +561,17 @@ __device__ __forceinline__ bool decode_group(int BH, int H, int G, int *b, int *
     return true;
 }
 
-// Enough workgroups to keep every CU busy: one per (image, head) when there
-// are many heads in the batch, else each head's query tiles are dealt to up
-// to G workgroups (tiles g, g+G, ...).
-constexpr int64_t kTargetWorkgroups = 3072;
+// One workgroup per (image, head) when the batch has at least as many heads
+// as the chip has CUs; otherwise each head's query tiles are dealt to G
+// workgroups (tiles g, g+G, ...), G = CUs / heads, at most one per tile.
+// Splitting further only adds workgroups that re-rank the image and re-stream
+// the head's K/V rows from L2.
+constexpr int64_t kComputeUnits = 256;
 
 int tile_groups(int B, int H, int max_seqlen) {
     const int ntiles = max_seqlen > 0 ? (max_seqlen + kQT - 1) / kQT : 1;
     const int64_t pairs = (int64_t)B * H;
-    const int64_t G = (kTargetWorkgroups + pairs - 1) / pairs;
+    const int64_t G = kComputeUnits / std::max<int64_t>(pairs, 1);
     return (int)std::max<int64_t>(1, std::min<int64_t>(G, ntiles));
 }
 
@@ -573,18 +586,21 @@ __global__ __launch_bounds__(kThreads, 4) void attn_fwd16(const uint16_t *__rest
                                                           const uint16_t *__restrict__ v,
                                                           uint16_t *__restrict__ o,
                                                           const int32_t *__restrict__ cu, int B,
-                                                          int H, int G, float c) {
+                                                          int H, int G, int max_seqlen, float c) {
     __shared__ __attribute__((aligned(16))) uint16_t sK[2 * kKC * 64];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2 * kD * 64];
     int b, h, g;
     if (!decode_group(B * H, H, G, &b, &h, &g)) return;
     const int seq0 = cu[b];
     const int L = cu[b + 1] - seq0;
-    if (L <= 0) return;
+    // an image longer than the caller's bound is outside the contract; it is
+    // skipped (its rows are left unwritten) rather than read out of range
+    if (L <= 0 || L > max_seqlen) return;
     const int64_t rs = (int64_t)H * kD;
-    const FlatRows R = {(int64_t)seq0 * rs + (int64_t)h * kD, rs};
-    if (c > 0.f) attend16<T, true>(q, k, v, o, R, L, c, g, G, sK, sV, nullptr);
-    else attend16<T, false>(q, k, v, o, R, L, c, g, G, sK, sV, nullptr);
+    const int64_t base = (int64_t)seq0 * rs + (int64_t)h * kD;
+    const FlatRows R = {(uint32_t)rs};
+    if (c > 0.f) attend16<T, true>(q + base, k + base, v + base, o + base, R, L, c, g, G, sK, sV, nullptr);
+    else attend16<T, false>(q + base, k + base, v + base, o + base, R, L, c, g, G, sK, sV, nullptr);
 }
 
 __global__ __launch_bounds__(kThreads) void attn_fwd32(const float *__restrict__ q,
@@ -592,17 +608,18 @@ __global__ __launch_bounds__(kThreads) void attn_fwd32(const float *__restrict__
                                                        const float *__restrict__ v,
                                                        float *__restrict__ o,
                                                        const int32_t *__restrict__ cu, int H,
-                                                       float c) {
+                                                       int max_seqlen, float c) {
     __shared__ __attribute__((aligned(16))) float sK[2 * kKC32 * kLd32];
     __shared__ __attribute__((aligned(16))) float sV[2 * kKC32 * kLd32];
     int b, h;
     decode_pair(H, &b, &h);
     const int seq0 = cu[b];
     const int L = cu[b + 1] - seq0;
-    if (L <= 0) return;
+    if (L <= 0 || L > max_seqlen) return;
     const int64_t rs = (int64_t)H * kD;
-    const FlatRows R = {(int64_t)seq0 * rs + (int64_t)h * kD, rs};
-    attend32(q, k, v, o, R, L, c, sK, sV, nullptr);
+    const int64_t base = (int64_t)seq0 * rs + (int64_t)h * kD;
+    const FlatRows R = {(uint32_t)rs};
+    attend32(q + base, k + base, v + base, o + base, R, L, c, sK, sV, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -620,12 +637,16 @@ __device__ __forceinline__ int rank_image(const uint8_t *__restrict__ keep_img, 
                                           int16_t *pos, uint64_t *keep_bits) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int nchunk = (N + 63) / 64;
+    // every load is issued before the first is used: positions past the end
+    // read the last byte of the row and are discarded
+    uint8_t byte[kMaxChunksPerWave];
+#pragma unroll
+    for (int i = 0; i < kMaxChunksPerWave; ++i)
+        byte[i] = keep_img[min(64 * (wid + kWaves * i) + lane, N - 1)];
     bool kept[kMaxChunksPerWave];
 #pragma unroll
-    for (int i = 0; i < kMaxChunksPerWave; ++i) {
-        const int n = 64 * (wid + kWaves * i) + lane;
-        kept[i] = n < N && keep_img[n] != 0;
-    }
+    for (int i = 0; i < kMaxChunksPerWave; ++i)
+        kept[i] = 64 * (wid + kWaves * i) + lane < N && byte[i] != 0;
     uint64_t m[kMaxChunksPerWave];
 #pragma unroll
     for (int i = 0; i < kMaxChunksPerWave; ++i) {
@@ -684,23 +705,34 @@ __global__ __launch_bounds__(kThreads, 4) void fused16(const uint16_t *__restric
     const int64_t rs = (int64_t)H * kD;
     const int64_t head0 = (int64_t)b * N * rs + (int64_t)h * kD;  // (b, 0, h)
     uint16_t *cls_head = cls ? cls + ((int64_t)b * H + h) * kD : nullptr;
-    if (g == 0)
-        zero_pruned<kD * 2 / 16>(keep_bits, N, out ? (u32x4 *)(out + head0) : nullptr,
-                                 rs * 2 / 16, (u32x4 *)cls_head);
-    if (L <= 0) return;
-    const PaddedRows R = {head0, rs, pos};
-    // the output row of query rank 0 is the CLS row iff position 0 was kept
-    uint16_t *cls_dst = (cls_head && pos[0] == 0) ? cls_head : nullptr;
-    if (!out) {
-        // CLS rows only: only the workgroup holding query tile 0 has work
-        if (!cls_dst || g != 0) return;
-        const int one_tile = (L + kQT - 1) / kQT;
-        if (c > 0.f) attend16<T, true>(q, k, v, nullptr, R, L, c, 0, one_tile, sK, sV, cls_dst);
-        else attend16<T, false>(q, k, v, nullptr, R, L, c, 0, one_tile, sK, sV, cls_dst);
-        return;
+    uint16_t *out_head = out ? out + head0 : nullptr;
+    if (L > 0) {
+        const PaddedRows R = {(uint32_t)rs, pos};
+        // the output row of query rank 0 is the CLS row iff position 0 was kept
+        uint16_t *cls_dst = (cls_head && pos[0] == 0) ? cls_head : nullptr;
+        int gg = g, GG = G;
+        bool run = true;
+        if (!out) {
+            // CLS rows only: only the workgroup holding query tile 0 has work,
+            // and it computes that tile alone
+            run = cls_dst && g == 0;
+            GG = (L + kQT - 1) / kQT;
+            gg = 0;
+        }
+        if (run) {
+            if (c > 0.f)
+                attend16<T, true>(q + head0, k + head0, v + head0, out_head, R, L, c, gg, GG, sK,
+                                  sV, cls_dst);
+            else
+                attend16<T, false>(q + head0, k + head0, v + head0, out_head, R, L, c, gg, GG, sK,
+                                   sV, cls_dst);
+        }
     }
-    if (c > 0.f) attend16<T, true>(q, k, v, out, R, L, c, g, G, sK, sV, cls_dst);
-    else attend16<T, false>(q, k, v, out, R, L, c, g, G, sK, sV, cls_dst);
+    // zeros for the pruned rows last, so that these stores are not waited
+    // for by the attention's loads
+    if (g == 0)
+        zero_pruned<kD * 2 / 16>(keep_bits, N, out_head ? (u32x4 *)out_head : nullptr, rs * 2 / 16,
+                                 (u32x4 *)cls_head);
 }
 
 __global__ __launch_bounds__(kThreads) void fused32(const float *__restrict__ q,
@@ -721,13 +753,15 @@ __global__ __launch_bounds__(kThreads) void fused32(const float *__restrict__ q,
     const int64_t rs = (int64_t)H * kD;
     const int64_t head0 = (int64_t)b * N * rs + (int64_t)h * kD;
     float *cls_head = cls ? cls + ((int64_t)b * H + h) * kD : nullptr;
-    zero_pruned<kD * 4 / 16>(keep_bits, N, out ? (u32x4 *)(out + head0) : nullptr, rs * 4 / 16,
+    float *out_head = out ? out + head0 : nullptr;
+    if (L > 0) {
+        const PaddedRows R = {(uint32_t)rs, pos};
+        float *cls_dst = (cls_head && pos[0] == 0) ? cls_head : nullptr;
+        if (out || cls_dst)
+            attend32(q + head0, k + head0, v + head0, out_head, R, L, c, sK, sV, cls_dst);
+    }
+    zero_pruned<kD * 4 / 16>(keep_bits, N, out_head ? (u32x4 *)out_head : nullptr, rs * 4 / 16,
                              (u32x4 *)cls_head);
-    if (L <= 0) return;
-    const PaddedRows R = {head0, rs, pos};
-    float *cls_dst = (cls_head && pos[0] == 0) ? cls_head : nullptr;
-    if (!out && !cls_dst) return;
-    attend32(q, k, v, out, R, L, c, sK, sV, cls_dst);
 }
 
 }  // namespace
@@ -740,17 +774,17 @@ hipError_t launch_attention(const AttnArgs &a, hipStream_t s) {
     case Elem::BF16:
         hipLaunchKernelGGL(attn_fwd16<__bf16>, dim3(grid), dim3(kThreads), 0, s,
                            (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
-                           (uint16_t *)a.o, a.cu, a.B, a.H, G, c);
+                           (uint16_t *)a.o, a.cu, a.B, a.H, G, a.max_seqlen, c);
         break;
     case Elem::F16:
         hipLaunchKernelGGL(attn_fwd16<_Float16>, dim3(grid), dim3(kThreads), 0, s,
                            (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
-                           (uint16_t *)a.o, a.cu, a.B, a.H, G, c);
+                           (uint16_t *)a.o, a.cu, a.B, a.H, G, a.max_seqlen, c);
         break;
     case Elem::F32:
         hipLaunchKernelGGL(attn_fwd32, dim3((unsigned)((int64_t)a.B * a.H)), dim3(kThreads), 0, s,
                            (const float *)a.q, (const float *)a.k, (const float *)a.v,
-                           (float *)a.o, a.cu, a.H, c);
+                           (float *)a.o, a.cu, a.H, a.max_seqlen, c);
         break;
     }
     return hipGetLastError();

@@ -116,6 +116,32 @@ inline emu_f32x4 emu_mfma_f32(float a, float b, emu_f32x4 c, int, int, int) { re
 #define __builtin_amdgcn_mfma_f32_16x16x32_f16 emu_mfma_f16
 #define __builtin_amdgcn_mfma_f32_16x16x4f32 emu_mfma_f32
 #define __builtin_amdgcn_exp2f exp2f
+#define __builtin_amdgcn_rcpf(X) (1.0f / (X))
+
+// readfirstlane: lane 0's value (every caller passes a wave-uniform value)
+template <typename T> inline T emu_readfirstlane(T v) { return emu_exchange_get(v, 0); }
+#define __builtin_amdgcn_readfirstlane(X) emu_readfirstlane(X)
+
+// v_permlane32_swap / v_permlane16_swap (gfx950): {new vdst, new vsrc} after
+// swapping the upper 32 lanes of vdst with the lower 32 of vsrc, resp. the odd
+// 16-lane rows of vdst with the even rows of vsrc.
+typedef uint32_t emu_u32x2 __attribute__((ext_vector_type(2)));
+inline emu_u32x2 emu_permlane_swap(uint32_t old, uint32_t src, int width) {
+    const uint32_t o_self = old, s_self = src;
+    const int l = emu_lane();
+    g_emu->slot[emu_wave()][l] = ((uint64_t)s_self << 32) | o_self;
+    emu_wave_sync();
+    auto o_at = [&](int i) { return (uint32_t)(g_emu->slot[emu_wave()][i] & 0xFFFFFFFFu); };
+    auto s_at = [&](int i) { return (uint32_t)(g_emu->slot[emu_wave()][i] >> 32); };
+    emu_u32x2 r;
+    const bool upper = (l / width) & 1;  // odd block of `width` lanes
+    r[0] = upper ? s_at(l - width) : o_at(l);
+    r[1] = upper ? s_at(l) : o_at(l + width);
+    emu_wave_sync();
+    return r;
+}
+#define __builtin_amdgcn_permlane32_swap(O, S, FI, BC) emu_permlane_swap((O), (S), 32)
+#define __builtin_amdgcn_permlane16_swap(O, S, FI, BC) emu_permlane_swap((O), (S), 16)
 
 void emu_launch(dim3 grid, dim3 block, const std::function<void()> &body);
 #define hipLaunchKernelGGL(K, G, Bk, SH, S, ...) emu_launch(dim3(G), dim3(Bk), [&] { K(__VA_ARGS__); })
