@@ -24,6 +24,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -39,6 +40,11 @@ import workloads  # noqa: E402
 from ragged_variable_length_amd import FusedPlan, rattn_init  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, datasheet
+# HBM traffic of the fused kernel measured with rocprofv3 counters (FETCH_SIZE,
+# WRITE_SIZE); valid only for the kernel sources it was taken on
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rattn_fused_hbm_traffic.txt")
+KERNEL_SOURCES = ("ragged_variable_length_amd/csrc/attention.hip",
+                  "ragged_variable_length_amd/csrc/internal.h")
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}  # dense
 ES = {"f32": 4, "f16": 2, "bf16": 2}
 METRIC = "ragged attn seqs/s + us/call at 80% pruning; % of MFMA/HBM roofline"
@@ -62,6 +68,94 @@ def attention_bytes(T: int, H: int, dtype: str) -> int:
 def attention_flops(lengths, H: int) -> int:
     """QK^T and PV: 2 * 2 * 64 flops per (query, key) pair per head."""
     return 4 * 64 * H * sum(L * L for L in lengths)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """Bytes per launch from the committed counter summary, or None when the
+    kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            lines = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+    except OSError:
+        return None
+    rec = {ln[0]: ln[1:] for ln in lines}
+    if rec.get("kernel_source_sha256", [None])[0] != kernel_source_hash():
+        return None
+    row = rec.get(workload)
+    if row is None or "traffic_bytes" not in row:
+        return None
+    return int(row[row.index("traffic_bytes") + 1])
+
+
+PMC_WORKLOADS = ("deit_s", "deit_b_384", "large_batch")
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str) -> str:
+    """Summary text of two rocprofv3 --pmc runs of `bench.py --pmc-target`
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch).  Each counter is scaled
+    by what it reads for the 256 MiB copy, and the three launches of each
+    workload are averaged."""
+    import csv
+
+    def per_kernel(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        copies = [float(r["Counter_Value"]) for r in rows
+                  if "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) > 100000]
+        fused = [float(r["Counter_Value"]) for r in rows if "fused16" in r["Kernel_Name"]]
+        return copies, fused
+
+    copy_bytes = 64 * 1024 * 1024 * 4
+    fc, ff = per_kernel(fetch_csv, "FETCH_SIZE")
+    wc, wf = per_kernel(write_csv, "WRITE_SIZE")
+    if len(ff) != 3 * len(PMC_WORKLOADS) or len(wf) != len(ff) or not fc or not wc:
+        raise RuntimeError("unexpected dispatches in the counter files")
+    f_scale = copy_bytes / 1024.0 / (sum(fc) / len(fc))
+    w_scale = copy_bytes / 1024.0 / (sum(wc) / len(wc))
+    out = [f"kernel_source_sha256 {kernel_source_hash()}",
+           f"fetch_scale {f_scale:.4f}",
+           f"write_scale {w_scale:.4f}"]
+    for i, name in enumerate(PMC_WORKLOADS):
+        w = workloads.by_name(name)
+        T = w.total_kept
+        alg = fused_bytes(T, w.B, w.N, w.H, w.dtype)
+        fk = sum(ff[3 * i:3 * i + 3]) / 3.0
+        wk = sum(wf[3 * i:3 * i + 3]) / 3.0
+        traffic = int(round((fk * f_scale + wk * w_scale) * 1024.0))
+        out.append(f"{w.name} fetch_kib {fk:.2f} write_kib {wk:.2f} traffic_bytes {traffic} "
+                   f"algorithmic_bytes {alg} ratio {traffic / alg:.3f}")
+    return "\n".join(out) + "\n"
+
+
+def pmc_target() -> None:
+    """Launches for the traffic counters (run under rocprofv3 --pmc): a plain
+    256 MiB device copy for calibration, then three rattn_fused launches on
+    each of the DeiT-S 80 %, DeiT-B 384 px and batch-512 workloads."""
+    rattn_init()
+    stream = torch.cuda.current_stream()
+    src = torch.randn(64 * 1024 * 1024, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[pmc] copy of {src.numel() * 4} bytes x3", flush=True)
+    del src, dst
+    for name in PMC_WORKLOADS:
+        r = Resident(workloads.by_name(name), stream)
+        for _ in range(3):
+            r.step()
+        torch.cuda.synchronize()
+        print(f"[pmc] {r.w.name}: rattn_fused x3, algorithmic bytes "
+              f"{fused_bytes(r.T, r.w.B, r.w.N, r.w.H, r.w.dtype)}", flush=True)
+        del r
 
 
 # ---------------------------------------------------------------------------
@@ -220,7 +314,8 @@ def large_configs(stream, launches: int) -> dict:
         nbytes = fused_bytes(r.T, w.B, w.N, w.H, w.dtype)
         flops = attention_flops(r.lengths, w.H)
         row = {"B": w.B, "N": w.N, "H": w.H, "dtype": w.dtype, "T": r.T,
-               "fused_bytes": nbytes, "attn_flops": flops}
+               "fused_bytes": nbytes, "attn_flops": flops,
+               "traffic_bytes": measured_traffic(w.name)}
         for cold in (False, True):
             us = kernel_time_us(r, launches, cold, flush)
             gbs = nbytes / (us * 1e-6) / 1e9
@@ -264,7 +359,14 @@ def main():
     ap.add_argument("--quick", action="store_true",
                     help="main metric only: no dispatch floors, no large configs, no CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-target", action="store_true",
+                    help="only the launches the traffic counters are read on, then exit")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the traffic summary of two counter runs, then exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        sys.stdout.write(summarize_pmc(*args.pmc_summary))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the path has no "
               "cross-GPU step and this build runs on a single MI355X; use --gpus 1.",
@@ -273,6 +375,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.pmc_target:
+        pmc_target()
+        return
     rattn_init()
     stream = torch.cuda.current_stream()
 
@@ -302,7 +407,8 @@ def main():
     achieved = nbytes / (kern_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": "rattn_fused", "achieved": round(achieved, 2),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
-                "traffic": None, "bytes_per_launch": nbytes, "avg_launch_us": round(kern_us, 3),
+                "traffic": measured_traffic(w.name), "bytes_per_launch": nbytes,
+                "avg_launch_us": round(kern_us, 3),
                 "avg_launch_us_from": "HIP events at the ends of the timed region / K "
                                       "(includes the gap between back-to-back dispatches)"}
 
