@@ -85,10 +85,12 @@ template <> struct Mma<_Float16> {
 __device__ __forceinline__ float max_across_groups(float x) {
     uint32_t u = __builtin_bit_cast(uint32_t, x);
     const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    x = fmaxf(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
+    x = __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)a[0]),
+                                      __builtin_bit_cast(float, (uint32_t)a[1]));
     u = __builtin_bit_cast(uint32_t, x);
     const auto b = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    return fmaxf(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]));
+    return __builtin_elementwise_maximum(__builtin_bit_cast(float, (uint32_t)b[0]),
+                                         __builtin_bit_cast(float, (uint32_t)b[1]));
 }
 
 __device__ __forceinline__ float sum_across_groups(float x) {
@@ -101,6 +103,10 @@ __device__ __forceinline__ float sum_across_groups(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max(a, b) as IEEE maximum (NaN-propagating, v_maximum3_f32 on gfx950):
+// unlike fmaxf it needs no canonicalizing of MFMA results before the compare.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
@@ -152,10 +158,18 @@ __device__ __forceinline__ u32x2 lds_read_tr(const uint16_t *p) {
 // global->LDS copies this wavefront issued have landed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// s_waitcnt vmcnt(N): all but the N most recent vector memory operations of
+// this wavefront have completed (N < 16).
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() {
+    static_assert(N >= 0 && N < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 // ---------------------------------------------------------------------------
 // 16-bit core: the query tiles g, g+G, ... of one (image, head)
 // ---------------------------------------------------------------------------
-template <typename T, bool kPos, typename Rows>
+template <typename T, bool kPos, int W, typename Rows>
 __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
                                          const uint16_t *__restrict__ kh,
                                          const uint16_t *__restrict__ vh,
@@ -169,34 +183,36 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
     const int col = lane & 15, grp = lane >> 4;
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
-    // Staging: wavefront w copies rows 16w .. 16w+15 of the K and V chunk, 8
-    // rows (1 KB) per DMA instruction; lane l fills row l/8, slot l%8.  Keys
-    // past the sequence end are not fetched: their K rows are masked out of
-    // the scores, their V rows are zeroed so 0-probability keys add exactly 0.
+    // Staging: a 64-key chunk is 16 DMA instructions of 8 rows (1 KB) -- 8
+    // for K, 8 for V -- dealt evenly to the W wavefronts; lane l fills row
+    // l/8, slot l%8 of its 8-row block.  Every instruction is issued with all
+    // lanes active, so each wavefront has exactly kDmaPerWave copies in
+    // flight per chunk and a partial s_waitcnt can wait for one chunk alone.
+    // Keys past the sequence end copy the last key's row: finite values whose
+    // scores are masked to -inf (K) and whose probability 0 makes them add
+    // exactly 0 (V).
+    constexpr int kQT16 = W * kQW;           // query rows per tile
+    constexpr int kDmaPerWave = 16 / W;
     const int srow = lane >> 3, sslot = lane & 7;
     auto stage = [&](int chunk, int buf) {
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-            const int row0 = 16 * wid + 8 * hb;
+        for (int i = 0; i < kDmaPerWave; ++i) {
+            const int idx = wid * kDmaPerWave + i;  // 0..7: K blocks, 8..15: V blocks
+            const bool is_v = idx >= 8;
+            const int row0 = 8 * (idx & 7);
             const int row = row0 + srow;
-            const int key = chunk * kKC + row;
-            uint16_t *kdst = sK + buf * (kKC * 64) + row0 * 64;
-            uint16_t *vdst = sV + buf * (kKC * 64) + row0 * 64;
-            if (key < L) {
-                const uint32_t ro = R.off(key);
-                __builtin_amdgcn_global_load_lds(kh + ro + 8 * kpiece(row, sslot), RATTN_LDS(kdst),
-                                                 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(vh + ro + 8 * vpiece(row, sslot), RATTN_LDS(vdst),
-                                                 16, 0, 0);
-            } else {
-                *(u32x4 *)(vdst + 8 * lane) = zero4;
-            }
+            const int key = min(chunk * kKC + row, L - 1);
+            uint16_t *dst = (is_v ? sV : sK) + buf * (kKC * 64) + row0 * 64;
+            const uint32_t ro = R.off(key);
+            const uint16_t *src = is_v ? vh + ro + 8 * vpiece(row, sslot)
+                                       : kh + ro + 8 * kpiece(row, sslot);
+            __builtin_amdgcn_global_load_lds(src, RATTN_LDS(dst), 16, 0, 0);
         }
     };
     // B operand of S^T = K Q^T for query tile `tile`: row `col` of this
     // wavefront's 16 rows, dims 8*grp .. +7 and 32 + 8*grp .. +7
     auto load_q = [&](int tile, u32x4 &a, u32x4 &b) {
-        const int qr = tile * kQT + wid * kQW + col;
+        const int qr = tile * kQT16 + wid * kQW + col;
         a = zero4;
         b = zero4;
         if (qr < L) {
@@ -206,28 +222,38 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
         }
     };
 
-    // This workgroup owns query tiles g, g+G, g+2G, ... of the sequence (G
-    // workgroups share one (image, head)).  Tiles and key chunks are both 64
-    // wide, so there are nch of each.  The work is one pipeline of steps
-    // (tile, chunk): the copy of the following step's K/V chunk -- the next
-    // chunk, or chunk 0 of the next tile -- and the next tile's Q rows are in
-    // flight while the current step computes.  With at most two chunks the
-    // double buffer holds the whole sequence, so only the first tile stages.
+    // This workgroup owns query tiles g, g+G, g+2G, ... (tiles of 16*W rows)
+    // of the sequence; G workgroups share one (image, head).  Keys come in
+    // nch chunks of 64.  The work is one pipeline of steps (tile, chunk): the
+    // copy of the following step's K/V chunk -- the next chunk, or chunk 0 of
+    // the next tile -- and the next tile's Q rows are in flight while the
+    // current step computes.  With at most two chunks the double buffer holds
+    // the whole sequence, so only the first tile stages.
     const int nch = (L + kKC - 1) / kKC;
-    if (g >= nch) return;
+    const int ntile = (L + kQT16 - 1) / kQT16;
+    if (g >= ntile) return;
     const bool resident = nch <= 2;
     int t = g, ch = 0, step = 0;
     u32x4 qf0, qf1, qn0 = zero4, qn1 = zero4;
     load_q(t, qf0, qf1);
     stage(0, 0);
-    wait_vmem();
+    if (resident && nch == 2) {
+        // both chunks in flight at once; wait for the Q rows and chunk 0
+        // only (loads complete in issue order)
+        stage(1, 1);
+        wait_vmem_but<kDmaPerWave>();
+    } else {
+        wait_vmem();
+    }
     __syncthreads();
 
     // all-ones A operand: its product with P^T gives P's row sums
     const V8 ones = __builtin_bit_cast(V8, u32x4{kOneBits, kOneBits, kOneBits, kOneBits});
     const int vr = 4 * grp + (col >> 2);
     const int vp = (col & 3) >> 1, vhalf = 4 * (col & 1);
-    float m = -INFINITY;
+    constexpr float kLag = 8.f;
+    const float lag = kPos ? kLag / c : 0.f;
+    float m = -INFINITY, mc = -INFINITY;
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0, acc3 = acc0, accl = acc0;
     while (true) {
         int nt = t, nc = ch + 1;
@@ -235,9 +261,9 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
             nt = t + G;
             nc = 0;
         }
-        const bool has_next = nt < nch;
+        const bool has_next = nt < ntile;
         const bool next_tile = has_next && nc == 0;
-        const bool load_next = resident ? step + 1 < nch : has_next;
+        const bool load_next = !resident && has_next;
         if (load_next) stage(nc, (step + 1) & 1);
         if (next_tile) load_q(nt, qn0, qn1);
 
@@ -248,7 +274,7 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
 
         // A wavefront whose 16 query rows all lie past the sequence end has
         // nothing to compute (it still stages and meets every barrier).
-        if (t * kQT + wid * kQW < L) {
+        if (t * kQT16 + wid * kQW < L) {
             // S^T for the 64 keys of the chunk.  Every block is computed:
             // rows of keys past the end hold stale LDS data whose scores are
             // replaced by -inf below, so no branch sits between the reads.
@@ -264,8 +290,12 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
             }
             if constexpr (kPos) {
                 // scale > 0: the largest score is the largest raw dot product,
-                // so the running max is kept in raw units and each probability
-                // is one fused multiply-add and one exp2.
+                // so the reference max m is kept in raw units and each
+                // probability is one fma and one exp2.  m may lag the running
+                // max by up to kLag / c (probabilities up to 2^kLag): the
+                // output and the row sum are rescaled only when some row's max
+                // grows past that, which after the first chunk is rare, and
+                // the final division cancels whichever reference was used.
                 if (valid < kKC) {
 #pragma unroll
                     for (int blk = 0; blk < 4; ++blk)
@@ -273,24 +303,26 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
                         for (int i = 0; i < 4; ++i)
                             if (16 * blk + 4 * grp + i >= valid) s[blk][i] = -INFINITY;
                 }
-                float mx = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
+                float mx = vmax(vmax(s[0][0], s[0][1]), vmax(s[0][2], s[0][3]));
 #pragma unroll
                 for (int blk = 1; blk < 4; ++blk)
-                    mx = fmaxf(fmaxf(mx, fmaxf(s[blk][0], s[blk][1])), fmaxf(s[blk][2], s[blk][3]));
+                    mx = vmax(vmax(mx, vmax(s[blk][0], s[blk][1])), vmax(s[blk][2], s[blk][3]));
                 mx = max_across_groups(mx);
-                const float mn = fmaxf(m, mx);
-                const float alpha = fast_exp2((m - mn) * c);
-                m = mn;
-                const float mc = mn * c;
+                if (__ballot(mx > m + lag)) {
+                    const float mn = vmax(m, mx);
+                    const float alpha = fast_exp2((m - mn) * c);
+                    m = mn;
+                    mc = mn * c;
+                    acc0 *= alpha;
+                    acc1 *= alpha;
+                    acc2 *= alpha;
+                    acc3 *= alpha;
+                    accl[0] *= alpha;
+                }
 #pragma unroll
                 for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) s[blk][i] = fast_exp2(__builtin_fmaf(s[blk][i], c, -mc));
-                acc0 *= alpha;
-                acc1 *= alpha;
-                acc2 *= alpha;
-                acc3 *= alpha;
-                accl[0] *= alpha;
             } else {
                 // scale <= 0 (degenerate but valid): scale first, then mask
 #pragma unroll
@@ -358,7 +390,7 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
 
         if (ch == nch - 1) {
             // tile t done: normalise and store; start the next tile afresh
-            const int qrow = t * kQT + wid * kQW + col;
+            const int qrow = t * kQT16 + wid * kQW + col;
             if (qrow < L) {
                 const float inv = __builtin_amdgcn_rcpf(accl[0]);
                 // lane holds o[qrow][16*dt + 4*grp + i], i = 0..3
@@ -382,13 +414,16 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
                 }
             }
             m = -INFINITY;
+            mc = -INFINITY;
             acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
             acc1 = acc0;
             acc2 = acc0;
             acc3 = acc0;
             accl = acc0;
         }
-        if (load_next) wait_vmem();
+        // the next step's chunk has landed: the one staged in this step, or,
+        // resident, chunk 1 staged up front
+        if (load_next || (resident && step == 0 && nch == 2)) wait_vmem();
         __syncthreads();
         if (!has_next) break;
         if (next_tile) {
@@ -562,17 +597,35 @@ __device__ __forceinline__ bool decode_group(int BH, int H, int G, int *b, int *
 }
 
 // One workgroup per (image, head) when the batch has at least as many heads
-// as the chip has CUs; otherwise each head's query tiles are dealt to G
-// workgroups (tiles g, g+G, ...), G = CUs / heads, at most one per tile.
-// Splitting further only adds workgroups that re-rank the image and re-stream
-// the head's K/V rows from L2.
+// as the chip has CUs; otherwise each head's query tiles (16*W rows) are
+// dealt to G workgroups (tiles g, g+G, ...), G = CUs / heads, at most one per
+// tile.  Splitting further only adds workgroups that re-rank the image and
+// re-stream the head's K/V rows.  In the fused kernel the last workgroup of
+// each head writes the pruned rows' zeros; while the chip has room
+// (`spare_for_zeros`) a head gets at least two workgroups so that those
+// stores overlap the attention of the first.
 constexpr int64_t kComputeUnits = 256;
 
-int tile_groups(int B, int H, int max_seqlen) {
-    const int ntiles = max_seqlen > 0 ? (max_seqlen + kQT - 1) / kQT : 1;
-    const int64_t pairs = (int64_t)B * H;
-    const int64_t G = kComputeUnits / std::max<int64_t>(pairs, 1);
-    return (int)std::max<int64_t>(1, std::min<int64_t>(G, ntiles));
+int tile_groups(int B, int H, int max_seqlen, int W, bool spare_for_zeros) {
+    const int rows = 16 * W;
+    const int ntiles = max_seqlen > 0 ? (max_seqlen + rows - 1) / rows : 1;
+    const int64_t pairs = std::max<int64_t>((int64_t)B * H, 1);
+    int64_t G = kComputeUnits / pairs;
+    if (spare_for_zeros && pairs < kComputeUnits) G = std::max<int64_t>(G, 2);
+    return (int)std::max<int64_t>(1, std::min<int64_t>(G, std::max(ntiles, spare_for_zeros ? 2 : 1)));
+}
+
+// Wavefronts per workgroup of the 16-bit kernels: a workgroup computes 16*W
+// query rows against each K/V chunk it stages, so a longer sequence gets more
+// wavefronts and its K/V rows are streamed fewer times.  Measured on MI355X at
+// 577 positions: 8 wavefronts beat 4 (K/V streamed half as often) and 16
+// (one workgroup per CU moving in lockstep leaves memory latency exposed).
+int waves_for(int max_seqlen) {
+#if defined(RATTN_FORCE_WAVES)
+    return RATTN_FORCE_WAVES;
+#else
+    return max_seqlen <= 256 ? 4 : 8;
+#endif
 }
 
 int64_t grid_for(int B, int H, int G) { return 8 * (((int64_t)B * H + 7) / 8) * G; }
@@ -580,13 +633,13 @@ int64_t grid_for(int B, int H, int G) { return 8 * (((int64_t)B * H + 7) / 8) * 
 // ---------------------------------------------------------------------------
 // kernels on the flat ragged buffer: one workgroup per (image, head)
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(kThreads, 4) void attn_fwd16(const uint16_t *__restrict__ q,
-                                                          const uint16_t *__restrict__ k,
-                                                          const uint16_t *__restrict__ v,
-                                                          uint16_t *__restrict__ o,
-                                                          const int32_t *__restrict__ cu, int B,
-                                                          int H, int G, int max_seqlen, float c) {
+template <typename T, int W>
+__global__ __launch_bounds__(64 * W, 4) void attn_fwd16(const uint16_t *__restrict__ q,
+                                                        const uint16_t *__restrict__ k,
+                                                        const uint16_t *__restrict__ v,
+                                                        uint16_t *__restrict__ o,
+                                                        const int32_t *__restrict__ cu, int B,
+                                                        int H, int G, int max_seqlen, float c) {
     __shared__ __attribute__((aligned(16))) uint16_t sK[2 * kKC * 64];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2 * kD * 64];
     int b, h, g;
@@ -599,8 +652,10 @@ __global__ __launch_bounds__(kThreads, 4) void attn_fwd16(const uint16_t *__rest
     const int64_t rs = (int64_t)H * kD;
     const int64_t base = (int64_t)seq0 * rs + (int64_t)h * kD;
     const FlatRows R = {(uint32_t)rs};
-    if (c > 0.f) attend16<T, true>(q + base, k + base, v + base, o + base, R, L, c, g, G, sK, sV, nullptr);
-    else attend16<T, false>(q + base, k + base, v + base, o + base, R, L, c, g, G, sK, sV, nullptr);
+    if (c > 0.f)
+        attend16<T, true, W>(q + base, k + base, v + base, o + base, R, L, c, g, G, sK, sV, nullptr);
+    else
+        attend16<T, false, W>(q + base, k + base, v + base, o + base, R, L, c, g, G, sK, sV, nullptr);
 }
 
 __global__ __launch_bounds__(kThreads) void attn_fwd32(const float *__restrict__ q,
@@ -626,40 +681,40 @@ __global__ __launch_bounds__(kThreads) void attn_fwd32(const float *__restrict__
 // fused kernels: padded in, padded out, one launch, one workgroup per
 // (image, head)
 // ---------------------------------------------------------------------------
-constexpr int kMaxChunksPerWave = (kMaxFusedN + 64 * kWaves - 1) / (64 * kWaves);
-
 // Kept positions of image b, in order, into pos[]; returns the count.  Every
 // wavefront loads the mask bytes of its 64-position chunks (chunk c belongs to
-// wave c % 4) in one round trip and ballots them; the ballots go to LDS as a
+// wave c % W) in one round trip and ballots them; the ballots go to LDS as a
 // keep bitmap, and after one exchange of per-chunk counts each wavefront
 // writes its kept positions at their ranks.
+template <int W>
 __device__ __forceinline__ int rank_image(const uint8_t *__restrict__ keep_img, int N,
                                           int16_t *pos, uint64_t *keep_bits) {
+    constexpr int kChunksPerWave = (kMaxFusedN + 64 * W - 1) / (64 * W);
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int nchunk = (N + 63) / 64;
     // every load is issued before the first is used: positions past the end
     // read the last byte of the row and are discarded
-    uint8_t byte[kMaxChunksPerWave];
+    uint8_t byte[kChunksPerWave];
 #pragma unroll
-    for (int i = 0; i < kMaxChunksPerWave; ++i)
-        byte[i] = keep_img[min(64 * (wid + kWaves * i) + lane, N - 1)];
-    bool kept[kMaxChunksPerWave];
+    for (int i = 0; i < kChunksPerWave; ++i)
+        byte[i] = keep_img[min(64 * (wid + W * i) + lane, N - 1)];
+    bool kept[kChunksPerWave];
 #pragma unroll
-    for (int i = 0; i < kMaxChunksPerWave; ++i)
-        kept[i] = 64 * (wid + kWaves * i) + lane < N && byte[i] != 0;
-    uint64_t m[kMaxChunksPerWave];
+    for (int i = 0; i < kChunksPerWave; ++i)
+        kept[i] = 64 * (wid + W * i) + lane < N && byte[i] != 0;
+    uint64_t m[kChunksPerWave];
 #pragma unroll
-    for (int i = 0; i < kMaxChunksPerWave; ++i) {
+    for (int i = 0; i < kChunksPerWave; ++i) {
         m[i] = __ballot(kept[i]);
-        const int chunk = wid + kWaves * i;
+        const int chunk = wid + W * i;
         if (lane == 0 && chunk < nchunk) keep_bits[chunk] = m[i];
     }
     __syncthreads();
     int total = 0;
     for (int cidx = 0; cidx < nchunk; ++cidx) total += __popcll(keep_bits[cidx]);
 #pragma unroll
-    for (int i = 0; i < kMaxChunksPerWave; ++i) {
-        const int chunk = wid + kWaves * i;
+    for (int i = 0; i < kChunksPerWave; ++i) {
+        const int chunk = wid + W * i;
         if (chunk >= nchunk) break;
         int before = 0;
         for (int cidx = 0; cidx < chunk; ++cidx) before += __popcll(keep_bits[cidx]);
@@ -672,13 +727,13 @@ __device__ __forceinline__ int rank_image(const uint8_t *__restrict__ keep_img, 
 // Zero rows of head h at the pruned positions of image b (and the CLS row
 // when position 0 was pruned), reading the keep bitmap from LDS; every
 // thread writes 16-byte pieces, 8 or 16 threads per 128/256-byte row.
-template <int kPiecesPerRow>
+template <int kPiecesPerRow, int kNThreads>
 __device__ __forceinline__ void zero_pruned(const uint64_t *keep_bits, int N,
                                             u32x4 *__restrict__ out_head0, int64_t row_vec,
                                             u32x4 *__restrict__ cls_head) {
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
     if (out_head0) {
-        for (int idx = threadIdx.x; idx < N * kPiecesPerRow; idx += kThreads) {
+        for (int idx = threadIdx.x; idx < N * kPiecesPerRow; idx += kNThreads) {
             const int n = idx / kPiecesPerRow, p = idx - n * kPiecesPerRow;
             if (!((keep_bits[n >> 6] >> (n & 63)) & 1ull)) out_head0[(int64_t)n * row_vec + p] = zero4;
         }
@@ -686,14 +741,14 @@ __device__ __forceinline__ void zero_pruned(const uint64_t *keep_bits, int N,
     if (cls_head && !(keep_bits[0] & 1ull) && threadIdx.x < kPiecesPerRow) cls_head[threadIdx.x] = zero4;
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads, 4) void fused16(const uint16_t *__restrict__ q,
-                                                       const uint16_t *__restrict__ k,
-                                                       const uint16_t *__restrict__ v,
-                                                       const uint8_t *__restrict__ keep,
-                                                       uint16_t *__restrict__ out,
-                                                       uint16_t *__restrict__ cls, int B, int N,
-                                                       int H, int G, float c) {
+template <typename T, int W>
+__global__ __launch_bounds__(64 * W, 4) void fused16(const uint16_t *__restrict__ q,
+                                                     const uint16_t *__restrict__ k,
+                                                     const uint16_t *__restrict__ v,
+                                                     const uint8_t *__restrict__ keep,
+                                                     uint16_t *__restrict__ out,
+                                                     uint16_t *__restrict__ cls, int B, int N,
+                                                     int H, int G, float c) {
     __shared__ __attribute__((aligned(16))) uint16_t sK[2 * kKC * 64];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2 * kD * 64];
     __shared__ int16_t pos[kMaxFusedN];
@@ -701,7 +756,7 @@ __global__ __launch_bounds__(kThreads, 4) void fused16(const uint16_t *__restric
     int b, h, g;
     if (!decode_group(B * H, H, G, &b, &h, &g)) return;
     const uint8_t *keep_img = keep + (int64_t)b * N;
-    const int L = rank_image(keep_img, N, pos, keep_bits);
+    const int L = rank_image<W>(keep_img, N, pos, keep_bits);
     const int64_t rs = (int64_t)H * kD;
     const int64_t head0 = (int64_t)b * N * rs + (int64_t)h * kD;  // (b, 0, h)
     uint16_t *cls_head = cls ? cls + ((int64_t)b * H + h) * kD : nullptr;
@@ -716,23 +771,23 @@ __global__ __launch_bounds__(kThreads, 4) void fused16(const uint16_t *__restric
             // CLS rows only: only the workgroup holding query tile 0 has work,
             // and it computes that tile alone
             run = cls_dst && g == 0;
-            GG = (L + kQT - 1) / kQT;
+            GG = (L + 16 * W - 1) / (16 * W);
             gg = 0;
         }
         if (run) {
             if (c > 0.f)
-                attend16<T, true>(q + head0, k + head0, v + head0, out_head, R, L, c, gg, GG, sK,
-                                  sV, cls_dst);
+                attend16<T, true, W>(q + head0, k + head0, v + head0, out_head, R, L, c, gg, GG,
+                                     sK, sV, cls_dst);
             else
-                attend16<T, false>(q + head0, k + head0, v + head0, out_head, R, L, c, gg, GG, sK,
-                                   sV, cls_dst);
+                attend16<T, false, W>(q + head0, k + head0, v + head0, out_head, R, L, c, gg, GG,
+                                      sK, sV, cls_dst);
         }
     }
-    // zeros for the pruned rows last, so that these stores are not waited
-    // for by the attention's loads
-    if (g == 0)
-        zero_pruned<kD * 2 / 16>(keep_bits, N, out_head ? (u32x4 *)out_head : nullptr, rs * 2 / 16,
-                                 (u32x4 *)cls_head);
+    // zeros for the pruned rows: by the last workgroup of the head, after its
+    // attention, so that the attention's loads never wait for these stores
+    if (g == G - 1)
+        zero_pruned<kD * 2 / 16, 64 * W>(keep_bits, N, out_head ? (u32x4 *)out_head : nullptr,
+                                         rs * 2 / 16, (u32x4 *)cls_head);
 }
 
 __global__ __launch_bounds__(kThreads) void fused32(const float *__restrict__ q,
@@ -749,7 +804,7 @@ __global__ __launch_bounds__(kThreads) void fused32(const float *__restrict__ q,
     int b, h;
     decode_pair(H, &b, &h);
     const uint8_t *keep_img = keep + (int64_t)b * N;
-    const int L = rank_image(keep_img, N, pos, keep_bits);
+    const int L = rank_image<kWaves>(keep_img, N, pos, keep_bits);
     const int64_t rs = (int64_t)H * kD;
     const int64_t head0 = (int64_t)b * N * rs + (int64_t)h * kD;
     float *cls_head = cls ? cls + ((int64_t)b * H + h) * kD : nullptr;
@@ -760,27 +815,56 @@ __global__ __launch_bounds__(kThreads) void fused32(const float *__restrict__ q,
         if (out || cls_dst)
             attend32(q + head0, k + head0, v + head0, out_head, R, L, c, sK, sV, cls_dst);
     }
-    zero_pruned<kD * 4 / 16>(keep_bits, N, out_head ? (u32x4 *)out_head : nullptr, rs * 4 / 16,
-                             (u32x4 *)cls_head);
+    zero_pruned<kD * 4 / 16, kThreads>(keep_bits, N, out_head ? (u32x4 *)out_head : nullptr,
+                                       rs * 4 / 16, (u32x4 *)cls_head);
+}
+
+template <typename T, int W>
+void launch_fwd16(const AttnArgs &a, float c, hipStream_t s) {
+    const int G = tile_groups(a.B, a.H, a.max_seqlen, W, false);
+    const unsigned grid = (unsigned)grid_for(a.B, a.H, G);
+    hipLaunchKernelGGL((attn_fwd16<T, W>), dim3(grid), dim3(64 * W), 0, s, (const uint16_t *)a.q,
+                       (const uint16_t *)a.k, (const uint16_t *)a.v, (uint16_t *)a.o, a.cu, a.B,
+                       a.H, G, a.max_seqlen, c);
+}
+
+template <typename T>
+void launch_fwd16_w(const AttnArgs &a, float c, hipStream_t s) {
+    switch (waves_for(a.max_seqlen)) {
+    case 4: launch_fwd16<T, 4>(a, c, s); break;
+    case 8: launch_fwd16<T, 8>(a, c, s); break;
+    default: launch_fwd16<T, 16>(a, c, s); break;
+    }
+}
+
+template <typename T, int W>
+void launch_fused16(const FusedArgs &a, float c, hipStream_t s) {
+    // without the padded output only tile 0 (the CLS row) is computed
+    const int G = a.out ? tile_groups(a.B, a.H, std::min(a.max_seqlen, a.N), W, true) : 1;
+    const unsigned grid = (unsigned)grid_for(a.B, a.H, G);
+    hipLaunchKernelGGL((fused16<T, W>), dim3(grid), dim3(64 * W), 0, s, (const uint16_t *)a.q,
+                       (const uint16_t *)a.k, (const uint16_t *)a.v, a.keep, (uint16_t *)a.out,
+                       (uint16_t *)a.cls, a.B, a.N, a.H, G, c);
+}
+
+template <typename T>
+void launch_fused16_w(const FusedArgs &a, float c, hipStream_t s) {
+    // the CLS-only mode computes one tile per head: the smallest workgroup
+    const int W = a.out ? waves_for(std::min(a.max_seqlen, a.N)) : 4;
+    switch (W) {
+    case 4: launch_fused16<T, 4>(a, c, s); break;
+    case 8: launch_fused16<T, 8>(a, c, s); break;
+    default: launch_fused16<T, 16>(a, c, s); break;
+    }
 }
 
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s) {
     const float c = a.scale * kLog2e;
-    const int G = tile_groups(a.B, a.H, a.max_seqlen);
-    const unsigned grid = (unsigned)grid_for(a.B, a.H, G);
     switch (a.dt) {
-    case Elem::BF16:
-        hipLaunchKernelGGL(attn_fwd16<__bf16>, dim3(grid), dim3(kThreads), 0, s,
-                           (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
-                           (uint16_t *)a.o, a.cu, a.B, a.H, G, a.max_seqlen, c);
-        break;
-    case Elem::F16:
-        hipLaunchKernelGGL(attn_fwd16<_Float16>, dim3(grid), dim3(kThreads), 0, s,
-                           (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
-                           (uint16_t *)a.o, a.cu, a.B, a.H, G, a.max_seqlen, c);
-        break;
+    case Elem::BF16: launch_fwd16_w<__bf16>(a, c, s); break;
+    case Elem::F16: launch_fwd16_w<_Float16>(a, c, s); break;
     case Elem::F32:
         hipLaunchKernelGGL(attn_fwd32, dim3((unsigned)((int64_t)a.B * a.H)), dim3(kThreads), 0, s,
                            (const float *)a.q, (const float *)a.k, (const float *)a.v,
@@ -792,20 +876,9 @@ hipError_t launch_attention(const AttnArgs &a, hipStream_t s) {
 
 hipError_t launch_fused(const FusedArgs &a, hipStream_t s) {
     const float c = a.scale * kLog2e;
-    // without the padded output only tile 0 (the CLS row) is computed
-    const int G = a.out ? tile_groups(a.B, a.H, std::min(a.max_seqlen, a.N)) : 1;
-    const unsigned grid = (unsigned)grid_for(a.B, a.H, G);
     switch (a.dt) {
-    case Elem::BF16:
-        hipLaunchKernelGGL(fused16<__bf16>, dim3(grid), dim3(kThreads), 0, s,
-                           (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
-                           a.keep, (uint16_t *)a.out, (uint16_t *)a.cls, a.B, a.N, a.H, G, c);
-        break;
-    case Elem::F16:
-        hipLaunchKernelGGL(fused16<_Float16>, dim3(grid), dim3(kThreads), 0, s,
-                           (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
-                           a.keep, (uint16_t *)a.out, (uint16_t *)a.cls, a.B, a.N, a.H, G, c);
-        break;
+    case Elem::BF16: launch_fused16_w<__bf16>(a, c, s); break;
+    case Elem::F16: launch_fused16_w<_Float16>(a, c, s); break;
     case Elem::F32:
         hipLaunchKernelGGL(fused32, dim3((unsigned)((int64_t)a.B * a.H)), dim3(kThreads), 0, s,
                            (const float *)a.q, (const float *)a.k, (const float *)a.v, a.keep,

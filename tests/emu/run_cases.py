@@ -142,6 +142,15 @@ def case_bounds():
     print("max_seqlen exact / N / 4N: same bits", flush=True)
 
 
+def case_long():
+    # longer than 256 positions: 16-wavefront workgroups, two 256-row query
+    # tiles, five 64-key chunks streamed through the double buffer
+    check_both(workloads.custom(2, 300, 1, "bf16", p_keep=0.95, seed=44, name="long_300_bf16"),
+               flat=False)
+    check_both(workloads.custom(1, 300, 1, "f16", p_keep=0.9, seed=45, name="long_300_f16"),
+               flat=False)
+
+
 def case_scan_large():
     # B*N above the single-launch limit: one-workgroup scan, then the gather;
     # pack and unpack only (the attention core is covered by the other cases)

@@ -73,6 +73,10 @@ def test_emulated_max_seqlen_bounds(emu_lib):
     _run(emu_lib, "bounds")
 
 
+def test_emulated_long_sequences_sixteen_waves(emu_lib):
+    _run(emu_lib, "long")
+
+
 def test_emulated_scan_over_single_launch_limit(emu_lib):
     _run(emu_lib, "scan_large")
 
