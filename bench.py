@@ -180,6 +180,7 @@ class BenchStep(ctypes.Structure):
                 ("stream", ctypes.c_void_p)]
 
 
+WHAT_FORWARD = 0
 WHAT_FUSED = 2
 _DT_CODE = {"f32": 0, "f16": 1, "bf16": 2}
 _timing = None
@@ -236,9 +237,38 @@ class Resident:
         return s
 
 
+class FlatResident:
+    """The flat ragged buffers of a workload (kept rows in order, prepared on
+    the host) and cu_seqlens, resident on the GPU, for rattn_forward alone."""
+
+    def __init__(self, w, stream):
+        self.w = w
+        dev = torch.device("cuda")
+        keep = w.keep != 0
+        self.flat = [t[keep].contiguous().to(dev) for t in (w.q, w.k, w.v)]
+        self.o = torch.empty_like(self.flat[0])
+        cu = torch.zeros(w.B + 1, dtype=torch.int32)
+        cu[1:] = torch.cumsum(keep.sum(dim=1), 0).to(torch.int32)
+        self.cu = cu.to(dev)
+        self.stream = stream
+        torch.cuda.synchronize()
+
+    def c_step(self) -> BenchStep:
+        s = BenchStep()
+        for i, t in enumerate(self.flat):
+            s.packed[i] = t.data_ptr()
+        s.o, s.cu = self.o.data_ptr(), self.cu.data_ptr()
+        s.B, s.N, s.H, s.max_seqlen = self.w.B, self.w.N, self.w.H, self.w.N
+        s.dtype, s.scale = _DT_CODE[self.w.dtype], self.w.scale
+        s.stream = self.stream.cuda_stream
+        return s
+
+
 def dispatch_floors(stream, iters: int, warmup: int) -> dict:
     """Host call -> completion (C++ steady_clock) at serving batch sizes 1-4,
-    80 % pruning, DeiT-B shape, plus the platform's empty-kernel floor."""
+    80 % pruning, DeiT-B shape: the one-launch rattn_fused (also enqueue-only
+    and replayed from a hipGraph) and rattn_forward alone on flat buffers,
+    plus the platform's empty-kernel floor."""
     lib = timing_lib()
     st = BenchStats()
     res = {}
@@ -258,9 +288,15 @@ def dispatch_floors(stream, iters: int, warmup: int) -> dict:
         row["fused_enqueue_us"] = st.as_dict()
         if lib.bench_graph_floor(ctypes.byref(cs), WHAT_FUSED, iters, warmup, ctypes.byref(st)) == 0:
             row["fused_graph_replay_sync_us"] = st.as_dict()
+        f = FlatResident(r.w, stream)
+        if lib.bench_call_floor(ctypes.byref(f.c_step()), WHAT_FORWARD, iters, warmup,
+                                ctypes.byref(st)):
+            raise RuntimeError("bench_call_floor (forward) failed")
+        row["forward_call_sync_us"] = st.as_dict()
         res[f"deit_b_B{B}_p80"] = row
-        print(f"[bench] dispatch floor B={B}: call+sync {row['fused_call_sync_us']['median_us']} us,"
-              f" enqueue {row['fused_enqueue_us']['median_us']} us", flush=True)
+        print(f"[bench] dispatch floor B={B}: fused call+sync {row['fused_call_sync_us']['median_us']} us,"
+              f" enqueue {row['fused_enqueue_us']['median_us']} us, rattn_forward alone call+sync "
+              f"{row['forward_call_sync_us']['median_us']} us", flush=True)
     return res
 
 
