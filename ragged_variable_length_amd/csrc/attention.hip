@@ -167,9 +167,13 @@ __device__ __forceinline__ void wait_vmem_but() {
 }
 
 // ---------------------------------------------------------------------------
-// 16-bit core: the query tiles g, g+G, ... of one (image, head)
+// 16-bit core: the query tiles g, g+G, ... of one (image, head).  W
+// wavefronts per workgroup, each owning QB blocks of 16 query rows (a tile is
+// 16*QB*W rows).  The blocks of one wavefront share every K and V operand
+// read from LDS, and their MFMA and softmax work is independent, so the
+// wavefront always has one block's arithmetic to overlap with the other's.
 // ---------------------------------------------------------------------------
-template <typename T, bool kPos, int W, typename Rows>
+template <typename T, bool kPos, int W, int QB, typename Rows>
 __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
                                          const uint16_t *__restrict__ kh,
                                          const uint16_t *__restrict__ vh,
@@ -191,7 +195,8 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
     // Keys past the sequence end copy the last key's row: finite values whose
     // scores are masked to -inf (K) and whose probability 0 makes them add
     // exactly 0 (V).
-    constexpr int kQT16 = W * kQW;           // query rows per tile
+    constexpr int kRowsPerWave = QB * kQW;
+    constexpr int kQT16 = W * kRowsPerWave;  // query rows per tile
     constexpr int kDmaPerWave = 16 / W;
     const int srow = lane >> 3, sslot = lane & 7;
     auto stage = [&](int chunk, int buf) {
@@ -209,32 +214,37 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
             __builtin_amdgcn_global_load_lds(src, RATTN_LDS(dst), 16, 0, 0);
         }
     };
-    // B operand of S^T = K Q^T for query tile `tile`: row `col` of this
-    // wavefront's 16 rows, dims 8*grp .. +7 and 32 + 8*grp .. +7
-    auto load_q = [&](int tile, u32x4 &a, u32x4 &b) {
-        const int qr = tile * kQT16 + wid * kQW + col;
-        a = zero4;
-        b = zero4;
-        if (qr < L) {
-            const uint16_t *src = qh + R.off(qr);
-            a = *(const u32x4 *)(src + 8 * grp);
-            b = *(const u32x4 *)(src + 32 + 8 * grp);
+    // B operand of S^T = K Q^T for block qb of query tile `tile`: row `col`
+    // of the block, dims 8*grp .. +7 and 32 + 8*grp .. +7
+    auto load_q = [&](int tile, u32x4 (&a)[QB], u32x4 (&b)[QB]) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int qr = tile * kQT16 + wid * kRowsPerWave + qb * kQW + col;
+            a[qb] = zero4;
+            b[qb] = zero4;
+            if (qr < L) {
+                const uint16_t *src = qh + R.off(qr);
+                a[qb] = *(const u32x4 *)(src + 8 * grp);
+                b[qb] = *(const u32x4 *)(src + 32 + 8 * grp);
+            }
         }
     };
 
-    // This workgroup owns query tiles g, g+G, g+2G, ... (tiles of 16*W rows)
-    // of the sequence; G workgroups share one (image, head).  Keys come in
-    // nch chunks of 64.  The work is one pipeline of steps (tile, chunk): the
-    // copy of the following step's K/V chunk -- the next chunk, or chunk 0 of
-    // the next tile -- and the next tile's Q rows are in flight while the
-    // current step computes.  With at most two chunks the double buffer holds
-    // the whole sequence, so only the first tile stages.
+    // This workgroup owns query tiles g, g+G, g+2G, ... of the sequence; G
+    // workgroups share one (image, head).  Keys come in nch chunks of 64.
+    // The work is one pipeline of steps (tile, chunk): the copy of the
+    // following step's K/V chunk -- the next chunk, or chunk 0 of the next
+    // tile -- and the next tile's Q rows are in flight while the current step
+    // computes.  With at most two chunks the double buffer holds the whole
+    // sequence, so only the first tile stages.
     const int nch = (L + kKC - 1) / kKC;
     const int ntile = (L + kQT16 - 1) / kQT16;
     if (g >= ntile) return;
     const bool resident = nch <= 2;
     int t = g, ch = 0, step = 0;
-    u32x4 qf0, qf1, qn0 = zero4, qn1 = zero4;
+    u32x4 qf0[QB], qf1[QB], qn0[QB], qn1[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) qn0[qb] = qn1[qb] = zero4;
     load_q(t, qf0, qf1);
     stage(0, 0);
     if (resident && nch == 2) {
@@ -253,8 +263,19 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
     const int vp = (col & 3) >> 1, vhalf = 4 * (col & 1);
     constexpr float kLag = 8.f;
     const float lag = kPos ? kLag / c : 0.f;
-    float m = -INFINITY, mc = -INFINITY;
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0, acc3 = acc0, accl = acc0;
+    float m[QB], mc[QB];
+    f32x4 acc[QB][4], accl[QB];
+    auto reset = [&]() {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            m[qb] = -INFINITY;
+            mc[qb] = -INFINITY;
+            accl[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) acc[qb][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    reset();
     while (true) {
         int nt = t, nc = ch + 1;
         if (nc == nch) {
@@ -272,88 +293,91 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
         const uint16_t *Vs = sV + buf * (kKC * 64);
         const int valid = L - ch * kKC;  // keys of this chunk inside the sequence
 
-        // A wavefront whose 16 query rows all lie past the sequence end has
+        // A wavefront whose query rows all lie past the sequence end has
         // nothing to compute (it still stages and meets every barrier).
-        if (t * kQT16 + wid * kQW < L) {
+        if (t * kQT16 + wid * kRowsPerWave < L) {
             // S^T for the 64 keys of the chunk.  Every block is computed:
-            // rows of keys past the end hold stale LDS data whose scores are
-            // replaced by -inf below, so no branch sits between the reads.
-            f32x4 s[4];
+            // rows of keys past the end hold copies of the last key, whose
+            // scores are replaced by -inf below, so no branch sits between
+            // the reads.  Each K operand serves all QB query blocks.
+            f32x4 s[QB][4];
 #pragma unroll
             for (int blk = 0; blk < 4; ++blk) {
                 const int row = 16 * blk + col;
                 const u32x4 a0 = *(const u32x4 *)(Ks + row * 64 + 8 * kpiece(row, grp));
                 const u32x4 a1 = *(const u32x4 *)(Ks + row * 64 + 8 * kpiece(row, 4 + grp));
-                f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                z = Mma<T>::run(__builtin_bit_cast(V8, a0), __builtin_bit_cast(V8, qf0), z);
-                s[blk] = Mma<T>::run(__builtin_bit_cast(V8, a1), __builtin_bit_cast(V8, qf1), z);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                    z = Mma<T>::run(__builtin_bit_cast(V8, a0), __builtin_bit_cast(V8, qf0[qb]), z);
+                    s[qb][blk] = Mma<T>::run(__builtin_bit_cast(V8, a1),
+                                             __builtin_bit_cast(V8, qf1[qb]), z);
+                }
             }
-            if constexpr (kPos) {
-                // scale > 0: the largest score is the largest raw dot product,
-                // so the reference max m is kept in raw units and each
-                // probability is one fma and one exp2.  m may lag the running
-                // max by up to kLag / c (probabilities up to 2^kLag): the
-                // output and the row sum are rescaled only when some row's max
-                // grows past that, which after the first chunk is rare, and
-                // the final division cancels whichever reference was used.
-                if (valid < kKC) {
+            if (valid < kKC) {
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
                     for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
-                            if (16 * blk + 4 * grp + i >= valid) s[blk][i] = -INFINITY;
-                }
-                float mx = vmax(vmax(s[0][0], s[0][1]), vmax(s[0][2], s[0][3]));
+                            if (16 * blk + 4 * grp + i >= valid) s[qb][blk][i] = -INFINITY;
+            }
 #pragma unroll
-                for (int blk = 1; blk < 4; ++blk)
-                    mx = vmax(vmax(mx, vmax(s[blk][0], s[blk][1])), vmax(s[blk][2], s[blk][3]));
-                mx = max_across_groups(mx);
-                if (__ballot(mx > m + lag)) {
-                    const float mn = vmax(m, mx);
-                    const float alpha = fast_exp2((m - mn) * c);
-                    m = mn;
-                    mc = mn * c;
-                    acc0 *= alpha;
-                    acc1 *= alpha;
-                    acc2 *= alpha;
-                    acc3 *= alpha;
-                    accl[0] *= alpha;
-                }
+            for (int qb = 0; qb < QB; ++qb) {
+                if constexpr (kPos) {
+                    // scale > 0: the largest score is the largest raw dot
+                    // product, so the reference max m is kept in raw units
+                    // and each probability is one fma and one exp2.  m may
+                    // lag the running max by up to kLag / c (probabilities up
+                    // to 2^kLag): the output and the row sum are rescaled only
+                    // when some row's max grows past that, which after the
+                    // first chunk is rare, and the final division cancels
+                    // whichever reference was used.
+                    float mx = vmax(vmax(s[qb][0][0], s[qb][0][1]), vmax(s[qb][0][2], s[qb][0][3]));
 #pragma unroll
-                for (int blk = 0; blk < 4; ++blk)
+                    for (int blk = 1; blk < 4; ++blk)
+                        mx = vmax(vmax(mx, vmax(s[qb][blk][0], s[qb][blk][1])),
+                                  vmax(s[qb][blk][2], s[qb][blk][3]));
+                    mx = max_across_groups(mx);
+                    if (__ballot(mx > m[qb] + lag)) {
+                        const float mn = vmax(m[qb], mx);
+                        const float alpha = fast_exp2((m[qb] - mn) * c);
+                        m[qb] = mn;
+                        mc[qb] = mn * c;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) s[blk][i] = fast_exp2(__builtin_fmaf(s[blk][i], c, -mc));
-            } else {
-                // scale <= 0 (degenerate but valid): scale first, then mask
-#pragma unroll
-                for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) s[blk][i] *= c;
-                if (valid < kKC) {
+                        for (int dt = 0; dt < 4; ++dt) acc[qb][dt] *= alpha;
+                        accl[qb][0] *= alpha;
+                    }
 #pragma unroll
                     for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
-                            if (16 * blk + 4 * grp + i >= valid) s[blk][i] = -INFINITY;
+                            s[qb][blk][i] = fast_exp2(__builtin_fmaf(s[qb][blk][i], c, -mc[qb]));
+                } else {
+                    // scale <= 0 (degenerate but valid): scale, then the
+                    // exact running max (masked scores stay -inf)
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float x = s[qb][blk][i] == -INFINITY ? -INFINITY : s[qb][blk][i] * c;
+                            s[qb][blk][i] = x;
+                            mx = fmaxf(mx, x);
+                        }
+                    mx = max_across_groups(mx);
+                    const float mn = fmaxf(m[qb], mx);
+                    const float alpha = fast_exp2(m[qb] - mn);
+                    m[qb] = mn;
+#pragma unroll
+                    for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) s[qb][blk][i] = fast_exp2(s[qb][blk][i] - mn);
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt) acc[qb][dt] *= alpha;
+                    accl[qb][0] *= alpha;
                 }
-                float mx = -INFINITY;
-#pragma unroll
-                for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[blk][i]);
-                mx = max_across_groups(mx);
-                const float mn = fmaxf(m, mx);
-                const float alpha = fast_exp2(m - mn);
-                m = mn;
-#pragma unroll
-                for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) s[blk][i] = fast_exp2(s[blk][i] - mn);
-                acc0 *= alpha;
-                acc1 *= alpha;
-                acc2 *= alpha;
-                acc3 *= alpha;
-                accl[0] *= alpha;
             }
 
             // O^T += V^T P^T.  Operand slot (lane group g, slot s) of the
@@ -362,64 +386,69 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
             // The V^T operand is read transposed out of row-major V: lane r of
             // group g addresses key 32*ks + 16*h + 4*g + r/4, dims 16*dt + 4*(r%4).
             // The row sums of the rounded P come from the same B operand
-            // against an all-ones A operand.
+            // against an all-ones A operand.  Each V operand serves all QB
+            // query blocks.
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 if (ks == 0 || valid > 32) {
-                    u32x4 pb;
-                    pb[0] = pack2<T>(s[2 * ks][0], s[2 * ks][1]);
-                    pb[1] = pack2<T>(s[2 * ks][2], s[2 * ks][3]);
-                    pb[2] = pack2<T>(s[2 * ks + 1][0], s[2 * ks + 1][1]);
-                    pb[3] = pack2<T>(s[2 * ks + 1][2], s[2 * ks + 1][3]);
-                    const V8 b = __builtin_bit_cast(V8, pb);
+                    V8 b[QB];
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) {
+                        u32x4 pb;
+                        pb[0] = pack2<T>(s[qb][2 * ks][0], s[qb][2 * ks][1]);
+                        pb[1] = pack2<T>(s[qb][2 * ks][2], s[qb][2 * ks][3]);
+                        pb[2] = pack2<T>(s[qb][2 * ks + 1][0], s[qb][2 * ks + 1][1]);
+                        pb[3] = pack2<T>(s[qb][2 * ks + 1][2], s[qb][2 * ks + 1][3]);
+                        b[qb] = __builtin_bit_cast(V8, pb);
+                    }
                     const int r0 = 32 * ks + vr, r1 = r0 + 16;
                     const uint16_t *v0 = Vs + r0 * 64 + vhalf;
                     const uint16_t *v1 = Vs + r1 * 64 + vhalf;
-                    f32x4 *accs[4] = {&acc0, &acc1, &acc2, &acc3};
 #pragma unroll
                     for (int dt = 0; dt < 4; ++dt) {
                         const u32x2 lo = lds_read_tr(v0 + 8 * vpiece(r0, 2 * dt + vp));
                         const u32x2 hi = lds_read_tr(v1 + 8 * vpiece(r1, 2 * dt + vp));
                         const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-                        *accs[dt] = Mma<T>::run(__builtin_bit_cast(V8, a), b, *accs[dt]);
+#pragma unroll
+                        for (int qb = 0; qb < QB; ++qb)
+                            acc[qb][dt] = Mma<T>::run(__builtin_bit_cast(V8, a), b[qb], acc[qb][dt]);
                     }
-                    accl = Mma<T>::run(ones, b, accl);
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) accl[qb] = Mma<T>::run(ones, b[qb], accl[qb]);
                 }
             }
         }
 
         if (ch == nch - 1) {
             // tile t done: normalise and store; start the next tile afresh
-            const int qrow = t * kQT16 + wid * kQW + col;
-            if (qrow < L) {
-                const float inv = __builtin_amdgcn_rcpf(accl[0]);
-                // lane holds o[qrow][16*dt + 4*grp + i], i = 0..3
-                const u32x2 w0 = {pack2<T>(acc0[0] * inv, acc0[1] * inv), pack2<T>(acc0[2] * inv, acc0[3] * inv)};
-                const u32x2 w1 = {pack2<T>(acc1[0] * inv, acc1[1] * inv), pack2<T>(acc1[2] * inv, acc1[3] * inv)};
-                const u32x2 w2 = {pack2<T>(acc2[0] * inv, acc2[1] * inv), pack2<T>(acc2[2] * inv, acc2[3] * inv)};
-                const u32x2 w3 = {pack2<T>(acc3[0] * inv, acc3[1] * inv), pack2<T>(acc3[2] * inv, acc3[3] * inv)};
-                if (oh) {
-                    uint16_t *orow = oh + R.off(qrow) + 4 * grp;
-                    *(u32x2 *)(orow) = w0;
-                    *(u32x2 *)(orow + 16) = w1;
-                    *(u32x2 *)(orow + 32) = w2;
-                    *(u32x2 *)(orow + 48) = w3;
-                }
-                if (cls_dst && qrow == 0) {
-                    uint16_t *crow = cls_dst + 4 * grp;
-                    *(u32x2 *)(crow) = w0;
-                    *(u32x2 *)(crow + 16) = w1;
-                    *(u32x2 *)(crow + 32) = w2;
-                    *(u32x2 *)(crow + 48) = w3;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const int qrow = t * kQT16 + wid * kRowsPerWave + qb * kQW + col;
+                if (qrow < L) {
+                    const float inv = __builtin_amdgcn_rcpf(accl[qb][0]);
+                    const f32x4 *a4 = acc[qb];
+                    // lane holds o[qrow][16*dt + 4*grp + i], i = 0..3
+                    const u32x2 w0 = {pack2<T>(a4[0][0] * inv, a4[0][1] * inv), pack2<T>(a4[0][2] * inv, a4[0][3] * inv)};
+                    const u32x2 w1 = {pack2<T>(a4[1][0] * inv, a4[1][1] * inv), pack2<T>(a4[1][2] * inv, a4[1][3] * inv)};
+                    const u32x2 w2 = {pack2<T>(a4[2][0] * inv, a4[2][1] * inv), pack2<T>(a4[2][2] * inv, a4[2][3] * inv)};
+                    const u32x2 w3 = {pack2<T>(a4[3][0] * inv, a4[3][1] * inv), pack2<T>(a4[3][2] * inv, a4[3][3] * inv)};
+                    if (oh) {
+                        uint16_t *orow = oh + R.off(qrow) + 4 * grp;
+                        *(u32x2 *)(orow) = w0;
+                        *(u32x2 *)(orow + 16) = w1;
+                        *(u32x2 *)(orow + 32) = w2;
+                        *(u32x2 *)(orow + 48) = w3;
+                    }
+                    if (cls_dst && qrow == 0) {
+                        uint16_t *crow = cls_dst + 4 * grp;
+                        *(u32x2 *)(crow) = w0;
+                        *(u32x2 *)(crow + 16) = w1;
+                        *(u32x2 *)(crow + 32) = w2;
+                        *(u32x2 *)(crow + 48) = w3;
+                    }
                 }
             }
-            m = -INFINITY;
-            mc = -INFINITY;
-            acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
-            acc1 = acc0;
-            acc2 = acc0;
-            acc3 = acc0;
-            accl = acc0;
+            reset();
         }
         // the next step's chunk has landed: the one staged in this step, or,
         // resident, chunk 1 staged up front
@@ -427,8 +456,11 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
         __syncthreads();
         if (!has_next) break;
         if (next_tile) {
-            qf0 = qn0;
-            qf1 = qn1;
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                qf0[qb] = qn0[qb];
+                qf1[qb] = qn1[qb];
+            }
         }
         t = nt;
         ch = nc;
@@ -606,8 +638,7 @@ __device__ __forceinline__ bool decode_group(int BH, int H, int G, int *b, int *
 // stores overlap the attention of the first.
 constexpr int64_t kComputeUnits = 256;
 
-int tile_groups(int B, int H, int max_seqlen, int W, bool spare_for_zeros) {
-    const int rows = 16 * W;
+int tile_groups(int B, int H, int max_seqlen, int rows, bool spare_for_zeros) {
     const int ntiles = max_seqlen > 0 ? (max_seqlen + rows - 1) / rows : 1;
     const int64_t pairs = std::max<int64_t>((int64_t)B * H, 1);
     int64_t G = kComputeUnits / pairs;
@@ -615,16 +646,27 @@ int tile_groups(int B, int H, int max_seqlen, int W, bool spare_for_zeros) {
     return (int)std::max<int64_t>(1, std::min<int64_t>(G, std::max(ntiles, spare_for_zeros ? 2 : 1)));
 }
 
-// Wavefronts per workgroup of the 16-bit kernels: a workgroup computes 16*W
-// query rows against each K/V chunk it stages, so a longer sequence gets more
-// wavefronts and its K/V rows are streamed fewer times.  Measured on MI355X at
-// 577 positions: 8 wavefronts beat 4 (K/V streamed half as often) and 16
-// (one workgroup per CU moving in lockstep leaves memory latency exposed).
-int waves_for(int max_seqlen) {
-#if defined(RATTN_FORCE_WAVES)
-    return RATTN_FORCE_WAVES;
+// Shape of the 16-bit workgroups: W wavefronts, each owning QB blocks of 16
+// query rows.  A workgroup computes 16*W*QB query rows against each K/V chunk
+// it stages, so longer sequences get larger tiles and stream their K/V rows
+// fewer times; two blocks per wavefront also halve the LDS operand reads per
+// score, at the cost of registers (three wavefronts per SIMD instead of four).
+struct Shape {
+    int W, QB;
+};
+
+Shape shape_for(int max_seqlen) {
+#if defined(RATTN_FORCE_W) && defined(RATTN_FORCE_QB)
+    (void)max_seqlen;
+    return Shape{RATTN_FORCE_W, RATTN_FORCE_QB};
 #else
-    return max_seqlen <= 256 ? 4 : 8;
+    // measured on MI355X (rattn_fused, back to back): up to 256 positions
+    // 4x1 is best (batch 512: 52 us; 4x2 56, 8x1 61); at 577 positions 4x2
+    // (56 us) beats 8x1 (60) and 4x1 (69): its 128-row tiles stream K/V three
+    // times instead of five, and at three workgroups per CU all 768 heads of
+    // a 64-image batch run in one round
+    if (max_seqlen <= 256) return Shape{4, 1};
+    return Shape{4, 2};
 #endif
 }
 
@@ -633,8 +675,8 @@ int64_t grid_for(int B, int H, int G) { return 8 * (((int64_t)B * H + 7) / 8) * 
 // ---------------------------------------------------------------------------
 // kernels on the flat ragged buffer: one workgroup per (image, head)
 // ---------------------------------------------------------------------------
-template <typename T, int W>
-__global__ __launch_bounds__(64 * W, 4) void attn_fwd16(const uint16_t *__restrict__ q,
+template <typename T, int W, int QB>
+__global__ __launch_bounds__(64 * W, QB == 1 ? 4 : 3) void attn_fwd16(const uint16_t *__restrict__ q,
                                                         const uint16_t *__restrict__ k,
                                                         const uint16_t *__restrict__ v,
                                                         uint16_t *__restrict__ o,
@@ -653,9 +695,11 @@ __global__ __launch_bounds__(64 * W, 4) void attn_fwd16(const uint16_t *__restri
     const int64_t base = (int64_t)seq0 * rs + (int64_t)h * kD;
     const FlatRows R = {(uint32_t)rs};
     if (c > 0.f)
-        attend16<T, true, W>(q + base, k + base, v + base, o + base, R, L, c, g, G, sK, sV, nullptr);
+        attend16<T, true, W, QB>(q + base, k + base, v + base, o + base, R, L, c, g, G, sK, sV,
+                                 nullptr);
     else
-        attend16<T, false, W>(q + base, k + base, v + base, o + base, R, L, c, g, G, sK, sV, nullptr);
+        attend16<T, false, W, QB>(q + base, k + base, v + base, o + base, R, L, c, g, G, sK, sV,
+                                  nullptr);
 }
 
 __global__ __launch_bounds__(kThreads) void attn_fwd32(const float *__restrict__ q,
@@ -741,8 +785,8 @@ __device__ __forceinline__ void zero_pruned(const uint64_t *keep_bits, int N,
     if (cls_head && !(keep_bits[0] & 1ull) && threadIdx.x < kPiecesPerRow) cls_head[threadIdx.x] = zero4;
 }
 
-template <typename T, int W>
-__global__ __launch_bounds__(64 * W, 4) void fused16(const uint16_t *__restrict__ q,
+template <typename T, int W, int QB>
+__global__ __launch_bounds__(64 * W, QB == 1 ? 4 : 3) void fused16(const uint16_t *__restrict__ q,
                                                      const uint16_t *__restrict__ k,
                                                      const uint16_t *__restrict__ v,
                                                      const uint8_t *__restrict__ keep,
@@ -771,15 +815,15 @@ __global__ __launch_bounds__(64 * W, 4) void fused16(const uint16_t *__restrict_
             // CLS rows only: only the workgroup holding query tile 0 has work,
             // and it computes that tile alone
             run = cls_dst && g == 0;
-            GG = (L + 16 * W - 1) / (16 * W);
+            GG = (L + 16 * W * QB - 1) / (16 * W * QB);
             gg = 0;
         }
         if (run) {
             if (c > 0.f)
-                attend16<T, true, W>(q + head0, k + head0, v + head0, out_head, R, L, c, gg, GG,
+                attend16<T, true, W, QB>(q + head0, k + head0, v + head0, out_head, R, L, c, gg, GG,
                                      sK, sV, cls_dst);
             else
-                attend16<T, false, W>(q + head0, k + head0, v + head0, out_head, R, L, c, gg, GG,
+                attend16<T, false, W, QB>(q + head0, k + head0, v + head0, out_head, R, L, c, gg, GG,
                                       sK, sV, cls_dst);
         }
     }
@@ -819,43 +863,42 @@ __global__ __launch_bounds__(kThreads) void fused32(const float *__restrict__ q,
                                        rs * 4 / 16, (u32x4 *)cls_head);
 }
 
-template <typename T, int W>
+template <typename T, int W, int QB>
 void launch_fwd16(const AttnArgs &a, float c, hipStream_t s) {
-    const int G = tile_groups(a.B, a.H, a.max_seqlen, W, false);
+    const int G = tile_groups(a.B, a.H, a.max_seqlen, 16 * W * QB, false);
     const unsigned grid = (unsigned)grid_for(a.B, a.H, G);
-    hipLaunchKernelGGL((attn_fwd16<T, W>), dim3(grid), dim3(64 * W), 0, s, (const uint16_t *)a.q,
-                       (const uint16_t *)a.k, (const uint16_t *)a.v, (uint16_t *)a.o, a.cu, a.B,
-                       a.H, G, a.max_seqlen, c);
+    hipLaunchKernelGGL((attn_fwd16<T, W, QB>), dim3(grid), dim3(64 * W), 0, s,
+                       (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
+                       (uint16_t *)a.o, a.cu, a.B, a.H, G, a.max_seqlen, c);
 }
 
 template <typename T>
-void launch_fwd16_w(const AttnArgs &a, float c, hipStream_t s) {
-    switch (waves_for(a.max_seqlen)) {
-    case 4: launch_fwd16<T, 4>(a, c, s); break;
-    case 8: launch_fwd16<T, 8>(a, c, s); break;
-    default: launch_fwd16<T, 16>(a, c, s); break;
-    }
+void launch_fwd16_shape(const AttnArgs &a, float c, hipStream_t s) {
+    const Shape sh = shape_for(a.max_seqlen);
+    if (sh.W == 4 && sh.QB == 1) launch_fwd16<T, 4, 1>(a, c, s);
+    else if (sh.W == 4) launch_fwd16<T, 4, 2>(a, c, s);
+    else if (sh.QB == 1) launch_fwd16<T, 8, 1>(a, c, s);
+    else launch_fwd16<T, 8, 2>(a, c, s);
 }
 
-template <typename T, int W>
+template <typename T, int W, int QB>
 void launch_fused16(const FusedArgs &a, float c, hipStream_t s) {
     // without the padded output only tile 0 (the CLS row) is computed
-    const int G = a.out ? tile_groups(a.B, a.H, std::min(a.max_seqlen, a.N), W, true) : 1;
+    const int G = a.out ? tile_groups(a.B, a.H, std::min(a.max_seqlen, a.N), 16 * W * QB, true) : 1;
     const unsigned grid = (unsigned)grid_for(a.B, a.H, G);
-    hipLaunchKernelGGL((fused16<T, W>), dim3(grid), dim3(64 * W), 0, s, (const uint16_t *)a.q,
-                       (const uint16_t *)a.k, (const uint16_t *)a.v, a.keep, (uint16_t *)a.out,
-                       (uint16_t *)a.cls, a.B, a.N, a.H, G, c);
+    hipLaunchKernelGGL((fused16<T, W, QB>), dim3(grid), dim3(64 * W), 0, s,
+                       (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, a.keep,
+                       (uint16_t *)a.out, (uint16_t *)a.cls, a.B, a.N, a.H, G, c);
 }
 
 template <typename T>
-void launch_fused16_w(const FusedArgs &a, float c, hipStream_t s) {
+void launch_fused16_shape(const FusedArgs &a, float c, hipStream_t s) {
     // the CLS-only mode computes one tile per head: the smallest workgroup
-    const int W = a.out ? waves_for(std::min(a.max_seqlen, a.N)) : 4;
-    switch (W) {
-    case 4: launch_fused16<T, 4>(a, c, s); break;
-    case 8: launch_fused16<T, 8>(a, c, s); break;
-    default: launch_fused16<T, 16>(a, c, s); break;
-    }
+    const Shape sh = a.out ? shape_for(std::min(a.max_seqlen, a.N)) : Shape{4, 1};
+    if (sh.W == 4 && sh.QB == 1) launch_fused16<T, 4, 1>(a, c, s);
+    else if (sh.W == 4) launch_fused16<T, 4, 2>(a, c, s);
+    else if (sh.QB == 1) launch_fused16<T, 8, 1>(a, c, s);
+    else launch_fused16<T, 8, 2>(a, c, s);
 }
 
 }  // namespace
@@ -863,8 +906,8 @@ void launch_fused16_w(const FusedArgs &a, float c, hipStream_t s) {
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s) {
     const float c = a.scale * kLog2e;
     switch (a.dt) {
-    case Elem::BF16: launch_fwd16_w<__bf16>(a, c, s); break;
-    case Elem::F16: launch_fwd16_w<_Float16>(a, c, s); break;
+    case Elem::BF16: launch_fwd16_shape<__bf16>(a, c, s); break;
+    case Elem::F16: launch_fwd16_shape<_Float16>(a, c, s); break;
     case Elem::F32:
         hipLaunchKernelGGL(attn_fwd32, dim3((unsigned)((int64_t)a.B * a.H)), dim3(kThreads), 0, s,
                            (const float *)a.q, (const float *)a.k, (const float *)a.v,
@@ -877,8 +920,8 @@ hipError_t launch_attention(const AttnArgs &a, hipStream_t s) {
 hipError_t launch_fused(const FusedArgs &a, hipStream_t s) {
     const float c = a.scale * kLog2e;
     switch (a.dt) {
-    case Elem::BF16: launch_fused16_w<__bf16>(a, c, s); break;
-    case Elem::F16: launch_fused16_w<_Float16>(a, c, s); break;
+    case Elem::BF16: launch_fused16_shape<__bf16>(a, c, s); break;
+    case Elem::F16: launch_fused16_shape<_Float16>(a, c, s); break;
     case Elem::F32:
         hipLaunchKernelGGL(fused32, dim3((unsigned)((int64_t)a.B * a.H)), dim3(kThreads), 0, s,
                            (const float *)a.q, (const float *)a.k, (const float *)a.v, a.keep,
