@@ -340,6 +340,23 @@ def kernel_time_us(r: Resident, launches: int, cold: bool, flush_buf=None) -> fl
     return times[len(times) // 2]
 
 
+def padded_comparison(r: Resident, launches: int) -> dict:
+    """The ragged kernel against its dense comparator (rattn_fused_padded,
+    same outputs): every image padded to the longest survivor, and to N (no
+    pruning gain at all), warm back-to-back averages."""
+    out = {"ragged_us": round(region_time_us(r, launches), 2)}
+    saved = r.step
+    for name, pad in (("padded_longest", max(r.lengths)), ("padded_n", r.w.N)):
+        plan = FusedPlan(r.q, r.k, r.v, r.keep, r.w.scale, out_padded=r.out, cls=r.cls,
+                         stream=r.stream, pad_len=max(pad, 1))
+        r.step = plan.run
+        us = region_time_us(r, launches)
+        out[f"{name}_us"] = round(us, 2)
+        out[f"ragged_speedup_vs_{name}"] = round(us / out["ragged_us"], 3)
+    r.step = saved
+    return out
+
+
 def large_configs(stream, launches: int) -> dict:
     out = {}
     flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device="cuda")
@@ -352,6 +369,7 @@ def large_configs(stream, launches: int) -> dict:
         row = {"B": w.B, "N": w.N, "H": w.H, "dtype": w.dtype, "T": r.T,
                "fused_bytes": nbytes, "attn_flops": flops,
                "traffic_bytes": measured_traffic(w.name)}
+        row["padded_comparator"] = padded_comparison(r, launches)
         for cold in (False, True):
             us = kernel_time_us(r, launches, cold, flush)
             gbs = nbytes / (us * 1e-6) / 1e9
@@ -361,8 +379,11 @@ def large_configs(stream, launches: int) -> dict:
                 "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                 "TFLOPs": round(tfl, 2), "mfma_frac": round(tfl / MFMA_PEAK_TFLOPS[w.dtype], 4)}
         out[name] = row
+        pc = row["padded_comparator"]
         print(f"[bench] {name}: warm {row['warm']['us']} us ({row['warm']['hbm_frac']:.3f} of HBM),"
-              f" cold {row['cold']['us']} us ({row['cold']['hbm_frac']:.3f})", flush=True)
+              f" cold {row['cold']['us']} us ({row['cold']['hbm_frac']:.3f}); padded comparator "
+              f"{pc['padded_longest_us']} us (longest survivor) / {pc['padded_n_us']} us (N)",
+              flush=True)
         del r
     del flush
     return out
@@ -463,6 +484,10 @@ def main():
         "roofline": roofline,
     }
     if not args.quick:
+        line["padded_comparator"] = padded_comparison(r, K)
+        pc = line["padded_comparator"]
+        print(f"[bench] {w.name}: ragged {pc['ragged_us']} us, padded to longest survivor "
+              f"{pc['padded_longest_us']} us, padded to N {pc['padded_n_us']} us", flush=True)
         side = torch.cuda.Stream()  # graph capture needs a non-default stream
         line["dispatch_floor"] = dispatch_floors(side, iters=1000, warmup=100)
         line["large_configs"] = large_configs(stream, launches=50)

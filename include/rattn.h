@@ -18,6 +18,9 @@
  *   [Pipeline]  same write-up, section on the integrated packing pipeline:
  *               compute cu_seqlens, copy surviving tokens with coalesced
  *               accesses into a contiguous flat tensor, attend, extract CLS.
+ *   [Padding]   same write-up, section on why pruning plus padding makes the
+ *               dense path regress: every image padded to the longest
+ *               survivor, the padding masked, the padded work still done.
  *
  * Conventions shared by every entry point:
  *   - All data pointers are DEVICE pointers owned by the caller (hipMalloc,
@@ -182,6 +185,23 @@ rattn_status rattn_unpack(const void *src, void *dst_padded, void *cls,
 rattn_status rattn_fused(const void *q, const void *k, const void *v, const uint8_t *keep,
                          void *out_padded, void *cls, int B, int N, int H, int head_dim,
                          int max_seqlen, float scale, rattn_dtype dt, void *stream);
+
+/*
+ * rattn_fused_padded -- [Padding]: the dense comparator of rattn_fused.  Every
+ * image is processed as if it had pad_len tokens: its kept tokens first, the
+ * rest padding whose keys are masked out and whose query rows are computed
+ * and discarded -- the work a padded, masked attention does when each image
+ * is padded to the longest survivor (pad_len = max kept count) or not pruned
+ * at all (pad_len = N).  The outputs are bit-for-bit those of rattn_fused
+ * (masked keys contribute exactly zero); only the work differs.
+ *
+ *   pad_len     1 <= pad_len <= N, and >= every image's kept count (an image
+ *               with more kept tokens is processed at its own length)
+ *   all other arguments as for rattn_fused (max_seqlen is pad_len)
+ */
+rattn_status rattn_fused_padded(const void *q, const void *k, const void *v, const uint8_t *keep,
+                                void *out_padded, void *cls, int B, int N, int H, int head_dim,
+                                int pad_len, float scale, rattn_dtype dt, void *stream);
 
 #ifdef __cplusplus
 }

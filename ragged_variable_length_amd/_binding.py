@@ -57,6 +57,8 @@ def load() -> ctypes.CDLL:
     lib.rattn_unpack.restype = i32
     lib.rattn_fused.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, f32, i32, P]
     lib.rattn_fused.restype = i32
+    lib.rattn_fused_padded.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, f32, i32, P]
+    lib.rattn_fused_padded.restype = i32
     _lib = lib
     return lib
 
@@ -208,3 +210,13 @@ def rattn_fused(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep: torch.T
     (C: rattn_fused)."""
     st = ext().fused(*fused_args(q, k, v, keep, scale, out_padded, cls, max_seqlen, stream))
     _check("rattn_fused", st)
+
+
+def rattn_fused_padded(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep: torch.Tensor,
+                       scale: float, pad_len: int, out_padded: torch.Tensor | None = None,
+                       cls: torch.Tensor | None = None, stream=None) -> None:
+    """The dense comparator of rattn_fused: every image processed at pad_len
+    tokens, padding masked; same outputs (C: rattn_fused_padded)."""
+    args = fused_args(q, k, v, keep, scale, out_padded, cls, int(pad_len), stream)
+    st = ext().fused_padded(*args)
+    _check("rattn_fused_padded", st)

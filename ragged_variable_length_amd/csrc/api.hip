@@ -168,9 +168,11 @@ rattn_status rattn_unpack(const void *src, void *dst_padded, void *cls, const ui
     return launch_unpack(a, (hipStream_t)stream) == hipSuccess ? RATTN_OK : RATTN_ERR_HIP;
 }
 
-rattn_status rattn_fused(const void *q, const void *k, const void *v, const uint8_t *keep,
-                         void *out_padded, void *cls, int B, int N, int H, int head_dim,
-                         int max_seqlen, float scale, rattn_dtype dt, void *stream) {
+namespace {
+
+rattn_status fused_common(const void *q, const void *k, const void *v, const uint8_t *keep,
+                          void *out_padded, void *cls, int B, int N, int H, int head_dim,
+                          int max_seqlen, int pad, float scale, rattn_dtype dt, void *stream) {
     if (elem_size(dt) == 0) return RATTN_ERR_INVALID_ARG;
     if (B < 0 || N < 1 || H < 1 || max_seqlen < 0 || !std::isfinite(scale))
         return RATTN_ERR_INVALID_ARG;
@@ -199,9 +201,27 @@ rattn_status rattn_fused(const void *q, const void *k, const void *v, const uint
     a.N = N;
     a.H = H;
     a.max_seqlen = max_seqlen;
+    a.pad = pad;
     a.scale = scale;
     a.dt = to_elem(dt);
     return launch_fused(a, (hipStream_t)stream) == hipSuccess ? RATTN_OK : RATTN_ERR_HIP;
+}
+
+}  // namespace
+
+rattn_status rattn_fused(const void *q, const void *k, const void *v, const uint8_t *keep,
+                         void *out_padded, void *cls, int B, int N, int H, int head_dim,
+                         int max_seqlen, float scale, rattn_dtype dt, void *stream) {
+    return fused_common(q, k, v, keep, out_padded, cls, B, N, H, head_dim, max_seqlen, 0, scale,
+                        dt, stream);
+}
+
+rattn_status rattn_fused_padded(const void *q, const void *k, const void *v, const uint8_t *keep,
+                                void *out_padded, void *cls, int B, int N, int H, int head_dim,
+                                int pad_len, float scale, rattn_dtype dt, void *stream) {
+    if (pad_len < 1 || pad_len > N) return RATTN_ERR_INVALID_ARG;
+    return fused_common(q, k, v, keep, out_padded, cls, B, N, H, head_dim, pad_len, pad_len,
+                        scale, dt, stream);
 }
 
 }  // extern "C"

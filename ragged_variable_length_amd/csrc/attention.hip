@@ -177,9 +177,12 @@ template <typename T, bool kPos, int W, int QB, typename Rows>
 __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
                                          const uint16_t *__restrict__ kh,
                                          const uint16_t *__restrict__ vh,
-                                         uint16_t *__restrict__ oh, const Rows &R, int L, float c,
-                                         int g, int G, uint16_t *sK, uint16_t *sV,
+                                         uint16_t *__restrict__ oh, const Rows &R, int L, int Lp,
+                                         float c, int g, int G, uint16_t *sK, uint16_t *sV,
                                          uint16_t *__restrict__ cls_dst) {
+    // Lp >= L is the length processed: L for ragged attention; for the padded
+    // comparator, the padded length, whose extra keys are masked and whose
+    // extra query rows are computed on zeros and discarded
     typedef typename Mma<T>::v8 V8;
     constexpr uint32_t kOneBits = Mma<T>::kOnePair;
     const int lane = threadIdx.x & 63;
@@ -237,8 +240,8 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
     // tile -- and the next tile's Q rows are in flight while the current step
     // computes.  With at most two chunks the double buffer holds the whole
     // sequence, so only the first tile stages.
-    const int nch = (L + kKC - 1) / kKC;
-    const int ntile = (L + kQT16 - 1) / kQT16;
+    const int nch = (Lp + kKC - 1) / kKC;
+    const int ntile = (Lp + kQT16 - 1) / kQT16;
     if (g >= ntile) return;
     const bool resident = nch <= 2;
     int t = g, ch = 0, step = 0;
@@ -291,11 +294,12 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
         const int buf = resident ? ch : (step & 1);
         const uint16_t *Ks = sK + buf * (kKC * 64);
         const uint16_t *Vs = sV + buf * (kKC * 64);
-        const int valid = L - ch * kKC;  // keys of this chunk inside the sequence
+        const int valid = L - ch * kKC;    // keys of this chunk inside the sequence
+        const int valid_p = Lp - ch * kKC; // keys of this chunk that are processed
 
         // A wavefront whose query rows all lie past the sequence end has
         // nothing to compute (it still stages and meets every barrier).
-        if (t * kQT16 + wid * kRowsPerWave < L) {
+        if (t * kQT16 + wid * kRowsPerWave < Lp) {
             // S^T for the 64 keys of the chunk.  Every block is computed:
             // rows of keys past the end hold copies of the last key, whose
             // scores are replaced by -inf below, so no branch sits between
@@ -390,7 +394,7 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
             // query blocks.
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                if (ks == 0 || valid > 32) {
+                if (ks == 0 || valid_p > 32) {
                     V8 b[QB];
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) {
@@ -474,8 +478,9 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
 template <typename Rows>
 __device__ __forceinline__ void attend32(const float *__restrict__ q, const float *__restrict__ k,
                                          const float *__restrict__ v, float *__restrict__ o,
-                                         const Rows &R, int L, float c, float *sK, float *sV,
-                                         float *__restrict__ cls_dst) {
+                                         const Rows &R, int L, int Lp, float c, float *sK,
+                                         float *sV, float *__restrict__ cls_dst) {
+    // Lp >= L: length processed (padded comparator), as in the 16-bit core
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
@@ -507,8 +512,8 @@ __device__ __forceinline__ void attend32(const float *__restrict__ q, const floa
         *(u32x4 *)(dv_ + key_b * kLd32 + 4 * c4) = vb;                                 \
     }
 
-    const int nch = (L + kKC32 - 1) / kKC32;
-    const int ntile = (L + kQT - 1) / kQT;
+    const int nch = (Lp + kKC32 - 1) / kKC32;
+    const int ntile = (Lp + kQT - 1) / kQT;
     const bool resident = nch <= 2;
     for (int t = 0; t < ntile; ++t) {
         // B operand of score step kk: Q[query col][4*kk + grp]
@@ -695,11 +700,11 @@ __global__ __launch_bounds__(64 * W, QB == 1 ? 4 : 3) void attn_fwd16(const uint
     const int64_t base = (int64_t)seq0 * rs + (int64_t)h * kD;
     const FlatRows R = {(uint32_t)rs};
     if (c > 0.f)
-        attend16<T, true, W, QB>(q + base, k + base, v + base, o + base, R, L, c, g, G, sK, sV,
+        attend16<T, true, W, QB>(q + base, k + base, v + base, o + base, R, L, L, c, g, G, sK, sV,
                                  nullptr);
     else
-        attend16<T, false, W, QB>(q + base, k + base, v + base, o + base, R, L, c, g, G, sK, sV,
-                                  nullptr);
+        attend16<T, false, W, QB>(q + base, k + base, v + base, o + base, R, L, L, c, g, G, sK,
+                                  sV, nullptr);
 }
 
 __global__ __launch_bounds__(kThreads) void attn_fwd32(const float *__restrict__ q,
@@ -718,7 +723,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd32(const float *__restrict__
     const int64_t rs = (int64_t)H * kD;
     const int64_t base = (int64_t)seq0 * rs + (int64_t)h * kD;
     const FlatRows R = {(uint32_t)rs};
-    attend32(q + base, k + base, v + base, o + base, R, L, c, sK, sV, nullptr);
+    attend32(q + base, k + base, v + base, o + base, R, L, L, c, sK, sV, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -792,7 +797,7 @@ __global__ __launch_bounds__(64 * W, QB == 1 ? 4 : 3) void fused16(const uint16_
                                                      const uint8_t *__restrict__ keep,
                                                      uint16_t *__restrict__ out,
                                                      uint16_t *__restrict__ cls, int B, int N,
-                                                     int H, int G, float c) {
+                                                     int H, int G, int pad, float c) {
     __shared__ __attribute__((aligned(16))) uint16_t sK[2 * kKC * 64];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2 * kD * 64];
     __shared__ int16_t pos[kMaxFusedN];
@@ -809,21 +814,23 @@ __global__ __launch_bounds__(64 * W, QB == 1 ? 4 : 3) void fused16(const uint16_
         const PaddedRows R = {(uint32_t)rs, pos};
         // the output row of query rank 0 is the CLS row iff position 0 was kept
         uint16_t *cls_dst = (cls_head && pos[0] == 0) ? cls_head : nullptr;
+        // padded comparator (pad > 0): every image processed at length pad
+        const int Lp = max(L, pad);
         int gg = g, GG = G;
         bool run = true;
         if (!out) {
             // CLS rows only: only the workgroup holding query tile 0 has work,
             // and it computes that tile alone
             run = cls_dst && g == 0;
-            GG = (L + 16 * W * QB - 1) / (16 * W * QB);
+            GG = (Lp + 16 * W * QB - 1) / (16 * W * QB);
             gg = 0;
         }
         if (run) {
             if (c > 0.f)
-                attend16<T, true, W, QB>(q + head0, k + head0, v + head0, out_head, R, L, c, gg, GG,
+                attend16<T, true, W, QB>(q + head0, k + head0, v + head0, out_head, R, L, Lp, c, gg, GG,
                                      sK, sV, cls_dst);
             else
-                attend16<T, false, W, QB>(q + head0, k + head0, v + head0, out_head, R, L, c, gg, GG,
+                attend16<T, false, W, QB>(q + head0, k + head0, v + head0, out_head, R, L, Lp, c, gg, GG,
                                       sK, sV, cls_dst);
         }
     }
@@ -840,7 +847,7 @@ __global__ __launch_bounds__(kThreads) void fused32(const float *__restrict__ q,
                                                     const uint8_t *__restrict__ keep,
                                                     float *__restrict__ out,
                                                     float *__restrict__ cls, int N, int H,
-                                                    float c) {
+                                                    int pad, float c) {
     __shared__ __attribute__((aligned(16))) float sK[2 * kKC32 * kLd32];
     __shared__ __attribute__((aligned(16))) float sV[2 * kKC32 * kLd32];
     __shared__ int16_t pos[kMaxFusedN];
@@ -857,7 +864,8 @@ __global__ __launch_bounds__(kThreads) void fused32(const float *__restrict__ q,
         const PaddedRows R = {(uint32_t)rs, pos};
         float *cls_dst = (cls_head && pos[0] == 0) ? cls_head : nullptr;
         if (out || cls_dst)
-            attend32(q + head0, k + head0, v + head0, out_head, R, L, c, sK, sV, cls_dst);
+            attend32(q + head0, k + head0, v + head0, out_head, R, L, max(L, pad), c, sK, sV,
+                     cls_dst);
     }
     zero_pruned<kD * 4 / 16, kThreads>(keep_bits, N, out_head ? (u32x4 *)out_head : nullptr,
                                        rs * 4 / 16, (u32x4 *)cls_head);
@@ -888,7 +896,7 @@ void launch_fused16(const FusedArgs &a, float c, hipStream_t s) {
     const unsigned grid = (unsigned)grid_for(a.B, a.H, G);
     hipLaunchKernelGGL((fused16<T, W, QB>), dim3(grid), dim3(64 * W), 0, s,
                        (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, a.keep,
-                       (uint16_t *)a.out, (uint16_t *)a.cls, a.B, a.N, a.H, G, c);
+                       (uint16_t *)a.out, (uint16_t *)a.cls, a.B, a.N, a.H, G, a.pad, c);
 }
 
 template <typename T>
@@ -925,7 +933,7 @@ hipError_t launch_fused(const FusedArgs &a, hipStream_t s) {
     case Elem::F32:
         hipLaunchKernelGGL(fused32, dim3((unsigned)((int64_t)a.B * a.H)), dim3(kThreads), 0, s,
                            (const float *)a.q, (const float *)a.k, (const float *)a.v, a.keep,
-                           (float *)a.out, (float *)a.cls, a.N, a.H, c);
+                           (float *)a.out, (float *)a.cls, a.N, a.H, a.pad, c);
         break;
     }
     return hipGetLastError();

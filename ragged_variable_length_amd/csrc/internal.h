@@ -70,6 +70,7 @@ struct FusedArgs {
     void *cls;              // [B, H, 64] (nullable)
     int B, N, H;
     int max_seqlen;
+    int pad;                // 0: ragged; > 0: padded comparator, every image at this length
     float scale;
     Elem dt;
 };

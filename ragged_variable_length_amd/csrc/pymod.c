@@ -177,6 +177,31 @@ static PyObject *py_fused(PyObject *self, PyObject *const *args, Py_ssize_t narg
                                        (rattn_dtype)dt, (void *)stream));
 }
 
+/* fused_padded(q, k, v, keep, out_padded|None, cls|None, B, N, H, head_dim, pad_len, scale,
+ *              dtype, stream) */
+static PyObject *py_fused_padded(PyObject *self, PyObject *const *args, Py_ssize_t nargs) {
+    (void)self;
+    if (nargs_is(nargs, 14, "fused_padded")) return NULL;
+    PTR(0, q);
+    PTR(1, k);
+    PTR(2, v);
+    PTR(3, keep);
+    PTR(4, out);
+    PTR(5, cls);
+    INT(6, B);
+    INT(7, N);
+    INT(8, H);
+    INT(9, head_dim);
+    INT(10, pad_len);
+    const double scale = PyFloat_AsDouble(args[11]);
+    if (scale == -1.0 && PyErr_Occurred()) return NULL;
+    INT(12, dt);
+    PTR(13, stream);
+    return PyLong_FromLong(rattn_fused_padded(q, k, v, (const uint8_t *)keep, (void *)out,
+                                              (void *)cls, B, N, H, head_dim, pad_len,
+                                              (float)scale, (rattn_dtype)dt, (void *)stream));
+}
+
 static PyMethodDef methods[] = {
     {"init", (PyCFunction)(void (*)(void))py_init, METH_FASTCALL, "rattn_init()"},
     {"status_string", (PyCFunction)(void (*)(void))py_status_string, METH_FASTCALL,
@@ -186,6 +211,8 @@ static PyMethodDef methods[] = {
     {"forward", (PyCFunction)(void (*)(void))py_forward, METH_FASTCALL, "rattn_forward(...)"},
     {"unpack", (PyCFunction)(void (*)(void))py_unpack, METH_FASTCALL, "rattn_unpack(...)"},
     {"fused", (PyCFunction)(void (*)(void))py_fused, METH_FASTCALL, "rattn_fused(...)"},
+    {"fused_padded", (PyCFunction)(void (*)(void))py_fused_padded, METH_FASTCALL,
+     "rattn_fused_padded(...)"},
     {NULL, NULL, 0, NULL}};
 
 static struct PyModuleDef module = {PyModuleDef_HEAD_INIT, "_rattn",

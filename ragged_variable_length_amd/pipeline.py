@@ -70,16 +70,20 @@ class FusedPlan:
     fixed when the plan is made (None = torch's current stream then).  The
     plan holds references to the tensors; their contents may change between
     runs, their storage may not.
+
+    With `pad_len` the plan runs the dense comparator rattn_fused_padded
+    instead (every image processed at pad_len tokens; same outputs).
     """
 
     def __init__(self, q, k, v, keep, scale: float, out_padded=None, cls=None,
-                 max_seqlen: int | None = None, stream=None):
-        self._args = _binding.fused_args(q, k, v, keep, scale, out_padded, cls, max_seqlen,
-                                         stream)
+                 max_seqlen: int | None = None, stream=None, pad_len: int | None = None):
+        bound = pad_len if pad_len is not None else max_seqlen
+        self._args = _binding.fused_args(q, k, v, keep, scale, out_padded, cls, bound, stream)
         self._tensors = (q, k, v, keep, out_padded, cls)
-        self._fn = _binding.ext().fused
+        self._name = "rattn_fused" if pad_len is None else "rattn_fused_padded"
+        self._fn = _binding.ext().fused if pad_len is None else _binding.ext().fused_padded
 
     def run(self) -> None:
         st = self._fn(*self._args)
         if st != 0:
-            raise RattnError("rattn_fused", st)
+            raise RattnError(self._name, st)

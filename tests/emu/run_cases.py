@@ -68,6 +68,9 @@ class CtypesBackend:
     def fused(self, *a):
         return self.lib.rattn_fused(*a)
 
+    def fused_padded(self, *a):
+        return self.lib.rattn_fused_padded(*a)
+
 
 def three_call(w, max_seqlen=None):
     pipe = rv.RaggedPipeline(w.B, w.N, w.H, w.q.dtype, device="cpu")
@@ -140,6 +143,25 @@ def case_bounds():
     b = three_call(w)
     assert np.array_equal(U.bits(a["po"]), U.bits(b["po"])), "max_seqlen bound changed bits"
     print("max_seqlen exact / N / 4N: same bits", flush=True)
+
+
+def case_padded():
+    # the dense comparator: every image processed at the padded length gives
+    # the ragged kernel's bits
+    for dt, H in (("bf16", 2), ("f32", 1)):
+        keep = _keep_lengths([1, 0, 17, 65, 100], 130, seed=46)
+        w = workloads.custom(5, 130, H, dt, keep=keep, seed=47, name=f"padded_{dt}")
+        ref_out, ref_cls = fused(w)
+        for pad in (max(w.kept_counts), w.N):
+            out = torch.empty_like(w.q)
+            cls = torch.empty((w.B, w.H, w.D), dtype=w.q.dtype)
+            for t in (out, cls):
+                t.view(torch.uint8).fill_(POISON)
+            rv.rattn_fused_padded(w.q, w.k, w.v, w.keep, w.scale, pad, out_padded=out, cls=cls)
+            assert np.array_equal(U.bits(out), U.bits(ref_out)), (w.name, pad, "out")
+            assert np.array_equal(U.bits(cls), U.bits(ref_cls)), (w.name, pad, "cls")
+        print(f"{w.name}: padded to {max(w.kept_counts)} and to {w.N}: bits equal to ragged",
+              flush=True)
 
 
 def case_long():

@@ -175,3 +175,13 @@ def test_extension_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         _binding.ext()
+
+
+def test_padded_comparator_argument_checks(lib):
+    f = lib.rattn_fused_padded
+    # pad_len outside [1, N]
+    assert f(A, A, A, A, A, None, 2, 10, 2, 64, 0, ctypes.c_float(0.125), BF16, None) == INVALID
+    assert f(A, A, A, A, A, None, 2, 10, 2, 64, 11, ctypes.c_float(0.125), BF16, None) == INVALID
+    # the fused checks apply too
+    assert f(A, A, A, A, A, None, 2, 10, 2, 63, 5, ctypes.c_float(0.125), BF16, None) == UNSUPPORTED
+    assert f(A, A, A, A, None, None, 2, 10, 2, 64, 5, ctypes.c_float(0.125), BF16, None) == INVALID

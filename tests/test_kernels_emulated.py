@@ -4,11 +4,12 @@ api.hip, pack.hip and attention.hip are compiled for x86 by clang++ against the
 emulation shim in tests/emu (one host thread per lane, wave intrinsics, MFMA,
 global_load_lds and the transposing LDS read emulated from their documented or
 measured lane layouts) with AddressSanitizer, and driven through the Python
-binding and the C ABI on host tensors.  Every entry point -- rattn_pack,
-rattn_forward, rattn_unpack, rattn_fused -- is checked against the oracle: the
-scan and the row movement bit-exact, attention within the per-dtype tolerances
-of `_gpu_util`, and the fused path bitwise equal to the three-call path.  Any
-out-of-bounds global or LDS access aborts the run.
+binding and the C ABI on host tensors.  Every entry point is checked:
+rattn_pack, rattn_forward and rattn_unpack against the oracle (the scan and
+the row movement bit-exact, attention within the per-dtype tolerances of
+`_gpu_util`), rattn_fused bitwise against the three-call path, and
+rattn_fused_padded bitwise against rattn_fused.  Any out-of-bounds global or
+LDS access aborts the run.
 
 These cases cover the three-call path, whose GPU parity tests are kept off the
 GPU (see test_gpu_parity.py).  The emulation does not model timing, memory
@@ -73,8 +74,12 @@ def test_emulated_max_seqlen_bounds(emu_lib):
     _run(emu_lib, "bounds")
 
 
-def test_emulated_long_sequences_sixteen_waves(emu_lib):
+def test_emulated_long_sequences(emu_lib):
     _run(emu_lib, "long")
+
+
+def test_emulated_padded_comparator_matches_ragged(emu_lib):
+    _run(emu_lib, "padded")
 
 
 def test_emulated_scan_over_single_launch_limit(emu_lib):
