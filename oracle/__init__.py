@@ -57,6 +57,8 @@ def _configure(lib):
     lib.oracle_attention.restype = i32
     lib.oracle_unpack.argtypes = [P, P, P, P, P, i32, i32, i64]
     lib.oracle_unpack.restype = i32
+    lib.oracle_repack.argtypes = [P, P, P, P, i32, i64, P]
+    lib.oracle_repack.restype = i64
     return lib
 
 
@@ -194,6 +196,29 @@ def unpack(src, keep, cu, want_padded: bool = True, want_cls: bool = True):
     if rc != 0:
         raise ValueError("oracle_unpack: cu_seqlens disagrees with the keep mask")
     return dst, cls
+
+
+def repack(src, keep2, cu):
+    """Flat [T, ...] rows of images cu, second keep flag per row [T] ->
+    (flat [T2, ...] of the rows kept again, cu2 int32 [B+1])."""
+    s = np.ascontiguousarray(_np(src))
+    k2 = np.ascontiguousarray(_u8(keep2)).reshape(-1)
+    cu = np.ascontiguousarray(cu, dtype=np.int32)
+    B = cu.shape[0] - 1
+    T = int(cu[-1])
+    assert s.shape[0] >= T and k2.shape[0] >= T
+    row_shape = s.shape[1:]
+    row_bytes = int(np.prod(row_shape)) * s.dtype.itemsize
+    T2 = int((k2[:T] != 0).sum())
+    out = _poisoned((T2,) + row_shape, s.dtype)
+    cu2 = np.full(B + 1, -1, dtype=np.int32)
+    sb = s.view(np.uint8).reshape(-1) if s.size else np.zeros(1, np.uint8)
+    ob = out.view(np.uint8).reshape(-1) if out.size else np.zeros(1, np.uint8)
+    n = _load().oracle_repack(_ptr(sb), _ptr(ob), _ptr(k2), _ptr(cu), B, row_bytes, _ptr(cu2))
+    if n < 0:
+        raise ValueError("oracle_repack: cu_seqlens decreases")
+    assert n == T2
+    return out, cu2
 
 
 def pipeline(w, rows=None, want_absw: bool = False):

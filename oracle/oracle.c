@@ -19,7 +19,9 @@
  *                kernel: no causal mask and no KV cache.
  *   [Pipeline]   same write-up, section on the integrated packing pipeline:
  *                compute cu_seqlens, copy the surviving tokens into a
- *                contiguous flat tensor, attend, then take the CLS token.
+ *                contiguous flat tensor, attend, then take the CLS token; the
+ *                pipeline is agnostic to the pruning method, including methods
+ *                that prune again at later blocks.
  *
  * Readings where the pages leave a step open (listed in the design doc):
  *   - keep mask is one byte per token, nonzero = kept;
@@ -75,6 +77,29 @@ int64_t oracle_pack(const uint8_t *src, uint8_t *dst, const uint8_t *keep,
                 r += 1;
             }
         }
+    return r;
+}
+
+/* [Pipeline], a second pruning stage: compact an already packed buffer under a
+ * second keep flag per flat row.  src is [T, row_bytes] with T = cu[B]; keep2
+ * is [T] (nonzero = keep); dst receives the kept rows, images in order and rows
+ * in order within each image; cu2[0..B] is the prefix sum of the new per-image
+ * counts.  Bitwise.  Returns the number of rows written, or -1 when cu
+ * decreases. */
+int64_t oracle_repack(const uint8_t *src, uint8_t *dst, const uint8_t *keep2,
+                      const int32_t *cu, int B, int64_t row_bytes, int32_t *cu2)
+{
+    int64_t r = 0;
+    cu2[0] = 0;
+    for (int b = 0; b < B; ++b) {
+        if (cu[b + 1] < cu[b]) return -1;
+        for (int64_t t = cu[b]; t < cu[b + 1]; ++t)
+            if (keep2[t] != 0) {
+                memcpy(dst + r * row_bytes, src + t * row_bytes, (size_t)row_bytes);
+                r += 1;
+            }
+        cu2[b + 1] = (int32_t)r;
+    }
     return r;
 }
 

@@ -316,3 +316,47 @@ def test_pipeline_on_tiny_workload():
     idx = np.nonzero(w.keep.reshape(-1).numpy())[0]
     assert np.array_equal(res["q"], flat[idx])
     assert res["o64"].shape == (cu[-1], w.H, w.D)
+
+
+# ---------------------------------------------------------------------------
+# re-pack (a second pruning stage on the packed buffer)
+# ---------------------------------------------------------------------------
+def test_repack_hand_fixture():
+    # two images of 3 and 2 rows; rows are single bytes equal to their index
+    src = np.arange(5, dtype=np.uint8).reshape(5, 1)
+    cu = np.array([0, 3, 5], np.int32)
+    keep2 = np.array([1, 0, 1, 0, 0], np.uint8)
+    out, cu2 = oracle.repack(src, keep2, cu)
+    assert out.reshape(-1).tolist() == [0, 2]
+    assert cu2.tolist() == [0, 2, 2]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_repack_composes_with_pack(seed):
+    """Pruning in two stages equals pruning once with both masks:
+    repack(pack(x, k1), k2 at the kept rows) == pack(x, k1 & k2), and the new
+    cu_seqlens is the scan of k1 & k2."""
+    rng = np.random.default_rng(seed)
+    B, N, H, D = 5, 23, 2, 8
+    x = rng.normal(size=(B, N, H, D)).astype(np.float32)
+    k1 = (rng.random((B, N)) < 0.6).astype(np.uint8)
+    k2 = (rng.random((B, N)) < 0.5).astype(np.uint8)
+    k1[2] = 0                      # an image emptied by the first stage
+    k2[3] = 0                      # and one by the second
+    cu1, _, _ = oracle.scan(k1)
+    flat = oracle.pack(x, k1)
+    k2_flat = oracle.pack(k2[..., None], k1).reshape(-1)
+    out, cu2 = oracle.repack(flat, k2_flat, cu1)
+    both = (k1 & k2).astype(np.uint8)
+    assert np.array_equal(out.view(np.uint8), oracle.pack(x, both).view(np.uint8))
+    assert cu2.tolist() == oracle.scan(both)[0].tolist()
+
+
+def test_repack_keep_all_is_identity_and_keep_none_empties():
+    rng = np.random.default_rng(7)
+    cu = np.array([0, 4, 4, 9], np.int32)
+    src = rng.integers(0, 2 ** 16, size=(9, 3), dtype=np.uint16)
+    out, cu2 = oracle.repack(src, np.ones(9, np.uint8), cu)
+    assert np.array_equal(out, src) and cu2.tolist() == cu.tolist()
+    out0, cu0 = oracle.repack(src, np.zeros(9, np.uint8), cu)
+    assert out0.shape[0] == 0 and cu0.tolist() == [0, 0, 0, 0]

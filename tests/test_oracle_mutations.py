@@ -28,6 +28,9 @@ MUTATIONS = {
                              "                r += (n > 0);\n            }\n        }\n    return r;"),
     "unpack_no_zero_fill": ("else memset(dst + t * row_bytes, 0, (size_t)row_bytes);", ""),
     "cls_from_last_row": ("if (cls && n == 0)", "if (cls && n == N - 1)"),
+    "repack_ignores_keep2": ("            if (keep2[t] != 0) {", "            if (1) {"),
+    "repack_cu_not_cumulative": ("        cu2[b + 1] = (int32_t)r;",
+                                 "        cu2[b + 1] = (int32_t)(r - (b > 0 ? cu2[b] : 0));"),
 }
 
 PINS = [
@@ -43,6 +46,8 @@ PINS = [
     (pins.test_dominant_logit_is_one_hot_and_finite, {}),
     (pins.test_matches_library_sdpa_per_image, dict(seed=11, B=3, N=9, H=2, D=64)),
     (pins.test_matches_brute_force_padded_masked, {"seed": 1}),
+    (pins.test_repack_hand_fixture, {}),
+    (pins.test_repack_composes_with_pack, {"seed": 0}),
 ]
 
 
