@@ -210,15 +210,16 @@ def repack(src, keep2, cu):
     row_shape = s.shape[1:]
     row_bytes = int(np.prod(row_shape)) * s.dtype.itemsize
     T2 = int((k2[:T] != 0).sum())
-    out = _poisoned((T2,) + row_shape, s.dtype)
+    # room for every row, so that the C code can never write past the buffer
+    out = _poisoned((max(T, 1),) + row_shape, s.dtype)
     cu2 = np.full(B + 1, -1, dtype=np.int32)
     sb = s.view(np.uint8).reshape(-1) if s.size else np.zeros(1, np.uint8)
-    ob = out.view(np.uint8).reshape(-1) if out.size else np.zeros(1, np.uint8)
+    ob = out.view(np.uint8).reshape(-1)
     n = _load().oracle_repack(_ptr(sb), _ptr(ob), _ptr(k2), _ptr(cu), B, row_bytes, _ptr(cu2))
     if n < 0:
         raise ValueError("oracle_repack: cu_seqlens decreases")
-    assert n == T2
-    return out, cu2
+    assert n == T2, "oracle_repack wrote an unexpected number of rows"
+    return out[:n].copy(), cu2
 
 
 def pipeline(w, rows=None, want_absw: bool = False):
