@@ -187,6 +187,28 @@ rattn_status rattn_fused(const void *q, const void *k, const void *v, const uint
                          int max_seqlen, float scale, rattn_dtype dt, void *stream);
 
 /*
+ * rattn_repack -- [Pipeline] with a later pruning stage: compact an already
+ * packed buffer under a second keep flag per flat row, so that the buffer
+ * stays ragged from one stage to the next.  Within each image the kept rows
+ * keep their order; images stay in order.  Bitwise row copies.
+ *
+ *   src         n_tensors (1..3) device pointers, [>= T, row_elems] of `dt`
+ *               each, T = cu_seqlens[B]
+ *   dst         n_tensors device pointers, [>= T2, row_elems] each (T2 = rows
+ *               kept; T is always enough); must not overlap src
+ *   keep2       device uint8 [>= T], 16-byte aligned: nonzero keeps the row
+ *   cu_seqlens  device int32 [B+1] of src
+ *   cu_seqlens_out  device int32 [B+1] (output), must not overlap cu_seqlens
+ *   total_dev   device int32 scalar (output, nullable): T2
+ * The longest image cannot grow, so a max_seqlen bound valid before the
+ * re-pack stays valid after it.
+ */
+rattn_status rattn_repack(const void *const *src, void *const *dst, int n_tensors,
+                          const uint8_t *keep2, const int32_t *cu_seqlens, int B, int row_elems,
+                          rattn_dtype dt, int32_t *cu_seqlens_out, int32_t *total_dev,
+                          void *stream);
+
+/*
  * rattn_fused_padded -- [Padding]: the dense comparator of rattn_fused.  Every
  * image is processed as if it had pad_len tokens: its kept tokens first, the
  * rest padding whose keys are masked out and whose query rows are computed

@@ -59,6 +59,8 @@ def load() -> ctypes.CDLL:
     lib.rattn_fused.restype = i32
     lib.rattn_fused_padded.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, f32, i32, P]
     lib.rattn_fused_padded.restype = i32
+    lib.rattn_repack.argtypes = [P, P, i32, P, P, i32, i32, i32, P, P, P]
+    lib.rattn_repack.restype = i32
     _lib = lib
     return lib
 
@@ -107,6 +109,18 @@ def _opt(t, name):
     return None if t is None else _dev(t, name)
 
 
+def _typed(t: torch.Tensor, name: str, dtype: torch.dtype) -> int:
+    """_dev for the index and mask arguments, whose element type the kernels
+    assume (int32 counts and offsets, uint8 flags)."""
+    if isinstance(t, torch.Tensor) and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return _dev(t, name)
+
+
+def _opt_typed(t, name, dtype):
+    return None if t is None else _typed(t, name, dtype)
+
+
 def _check(fn: str, status: int) -> None:
     if status != RATTN_OK:
         raise RattnError(fn, status)
@@ -134,9 +148,9 @@ def rattn_pack(srcs, dsts, keep: torch.Tensor, cu_seqlens: torch.Tensor,
     for x in row:
         row_elems *= int(x)
     st = ext().pack([_dev(s, "src") for s in srcs], [_dev(d, "dst") for d in dsts],
-                    _dev(keep, "keep"), B, N, row_elems, _DTYPE_CODE[dt],
-                    _dev(cu_seqlens, "cu_seqlens"), _opt(max_seqlen, "max_seqlen"),
-                    _opt(total, "total"), _stream(stream, keep))
+                    _typed(keep, "keep", torch.uint8), B, N, row_elems, _DTYPE_CODE[dt],
+                    _typed(cu_seqlens, "cu_seqlens", torch.int32), _opt_typed(max_seqlen, "max_seqlen", torch.int32),
+                    _opt_typed(total, "total", torch.int32), _stream(stream, keep))
     _check("rattn_pack", st)
 
 
@@ -151,7 +165,7 @@ def rattn_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
     _, H, D = q.shape
     B = cu_seqlens.shape[0] - 1
     st = ext().forward(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"),
-                       _dev(cu_seqlens, "cu_seqlens"), B, int(max_seqlen), H, D, float(scale),
+                       _typed(cu_seqlens, "cu_seqlens", torch.int32), B, int(max_seqlen), H, D, float(scale),
                        _DTYPE_CODE[q.dtype], _stream(stream, q))
     _check("rattn_forward", st)
 
@@ -173,7 +187,7 @@ def rattn_unpack(src: torch.Tensor, keep: torch.Tensor, cu_seqlens: torch.Tensor
     if cls is not None and tuple(cls.shape) != (B,) + tuple(src.shape[1:]):
         raise ValueError("rattn_unpack: cls must be [B, *row]")
     st = ext().unpack(_dev(src, "src"), _opt(dst_padded, "dst_padded"), _opt(cls, "cls"),
-                      _dev(keep, "keep"), _dev(cu_seqlens, "cu_seqlens"), B, N, row_elems,
+                      _typed(keep, "keep", torch.uint8), _typed(cu_seqlens, "cu_seqlens", torch.int32), B, N, row_elems,
                       _DTYPE_CODE[src.dtype], _stream(stream, src))
     _check("rattn_unpack", st)
 
@@ -197,7 +211,7 @@ def fused_args(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep: torch.Te
     if cls is not None and (tuple(cls.shape) != (B, H, D) or cls.dtype != dt):
         raise ValueError("rattn_fused: cls must be [B, H, head_dim] of q's dtype")
     ms = N if max_seqlen is None else int(max_seqlen)
-    return (_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(keep, "keep"),
+    return (_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _typed(keep, "keep", torch.uint8),
             _opt(out_padded, "out_padded"), _opt(cls, "cls"), B, N, H, D, ms, float(scale),
             _DTYPE_CODE[dt], _stream(stream, q))
 
@@ -220,3 +234,29 @@ def rattn_fused_padded(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep: 
     args = fused_args(q, k, v, keep, scale, out_padded, cls, int(pad_len), stream)
     st = ext().fused_padded(*args)
     _check("rattn_fused_padded", st)
+
+
+def rattn_repack(srcs, dsts, keep2: torch.Tensor, cu_seqlens: torch.Tensor,
+                 cu_seqlens_out: torch.Tensor, total: torch.Tensor | None = None,
+                 stream=None) -> None:
+    """Compact 1-3 flat [T, ...] buffers under a second keep flag per row into
+    flat [T2, ...] buffers, writing the new cu_seqlens (C: rattn_repack)."""
+    srcs, dsts = list(srcs), list(dsts)
+    if not 1 <= len(srcs) == len(dsts) <= 3:
+        raise ValueError("rattn_repack takes 1-3 (src, dst) pairs")
+    dt = srcs[0].dtype
+    row = srcs[0].shape[1:]
+    for s_, d_ in zip(srcs, dsts):
+        if s_.dtype != dt or d_.dtype != dt or s_.shape[1:] != row or d_.shape[1:] != row:
+            raise ValueError("rattn_repack: inconsistent shapes or dtypes")
+    row_elems = 1
+    for x in row:
+        row_elems *= int(x)
+    B = cu_seqlens.shape[0] - 1
+    if tuple(cu_seqlens_out.shape) != (B + 1,):
+        raise ValueError("rattn_repack: cu_seqlens_out must be [B+1]")
+    st = ext().repack([_dev(s_, "src") for s_ in srcs], [_dev(d_, "dst") for d_ in dsts],
+                      _typed(keep2, "keep2", torch.uint8), _typed(cu_seqlens, "cu_seqlens", torch.int32), B, row_elems,
+                      _DTYPE_CODE[dt], _typed(cu_seqlens_out, "cu_seqlens_out", torch.int32),
+                      _opt_typed(total, "total", torch.int32), _stream(stream, keep2))
+    _check("rattn_repack", st)

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "librattn.so")
-SOURCES = ["api.hip", "pack.hip", "attention.hip"]
+SOURCES = ["api.hip", "pack.hip", "attention.hip", "repack.hip"]
 # host-side timing loops used by bench.py (links librattn.so; not product ABI)
 BENCH_LIB = os.path.join(HERE, "librattn_bench.so")
 BENCH_SOURCES = ["bench_host.hip"]

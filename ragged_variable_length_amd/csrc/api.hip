@@ -168,6 +168,40 @@ rattn_status rattn_unpack(const void *src, void *dst_padded, void *cls, const ui
     return launch_unpack(a, (hipStream_t)stream) == hipSuccess ? RATTN_OK : RATTN_ERR_HIP;
 }
 
+rattn_status rattn_repack(const void *const *src, void *const *dst, int n_tensors,
+                          const uint8_t *keep2, const int32_t *cu_seqlens, int B, int row_elems,
+                          rattn_dtype dt, int32_t *cu_seqlens_out, int32_t *total_dev,
+                          void *stream) {
+    if (n_tensors < 1 || n_tensors > RATTN_MAX_TENSORS || !src || !dst) return RATTN_ERR_INVALID_ARG;
+    if (B < 0) return RATTN_ERR_INVALID_ARG;
+    const int rv = row_vectors(row_elems, dt);
+    if (rv == 0) return RATTN_ERR_INVALID_ARG;
+    if (B == 0) return RATTN_OK;
+    if (!keep2 || !aligned16(keep2) || !cu_seqlens || !aligned4(cu_seqlens) || !cu_seqlens_out ||
+        !aligned4(cu_seqlens_out) || (total_dev && !aligned4(total_dev)))
+        return RATTN_ERR_INVALID_ARG;
+    if (cu_seqlens_out == cu_seqlens) return RATTN_ERR_INVALID_ARG;
+    for (int i = 0; i < n_tensors; ++i) {
+        if (!src[i] || !dst[i] || !aligned16(src[i]) || !aligned16(dst[i]) || src[i] == dst[i])
+            return RATTN_ERR_INVALID_ARG;
+    }
+    rattn_status st = rattn_init();
+    if (st != RATTN_OK) return st;
+    RepackArgs a;
+    for (int i = 0; i < kMaxTensors; ++i) {
+        a.src[i] = i < n_tensors ? (const u32x4 *)src[i] : nullptr;
+        a.dst[i] = i < n_tensors ? (u32x4 *)dst[i] : nullptr;
+    }
+    a.keep2 = keep2;
+    a.cu = cu_seqlens;
+    a.cu2 = cu_seqlens_out;
+    a.total_out = total_dev;
+    a.B = B;
+    a.row_vec = rv;
+    a.n_tensors = n_tensors;
+    return launch_repack(a, (hipStream_t)stream) == hipSuccess ? RATTN_OK : RATTN_ERR_HIP;
+}
+
 namespace {
 
 rattn_status fused_common(const void *q, const void *k, const void *v, const uint8_t *keep,

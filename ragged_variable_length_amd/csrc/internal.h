@@ -27,6 +27,25 @@ inline Chunking chunking_for(int N) {
     return c;
 }
 
+// Moves 16-byte vector `so` of each of NT source tensors to vector `d` of the
+// matching destination.  The tensor count is a compile-time constant on
+// purpose: behind a run-time branch on the count (1, 2 or 3 tensors), the
+// gfx950 code generator of ROCm 7.2 structurized the three cases so that on
+// the three-tensor path the register holding the second destination's base
+// address was never written, and that store went to an unrelated address.
+// Straight-line code per count has no such join.
+template <int NT>
+__device__ __forceinline__ void copy_vec(const u32x4 *const (&src)[kMaxTensors],
+                                         u32x4 *const (&dst)[kMaxTensors], int64_t so,
+                                         int64_t d) {
+    static_assert(NT >= 1 && NT <= kMaxTensors, "1-3 tensors");
+    u32x4 x[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) x[t] = src[t][so];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) dst[t][d] = x[t];
+}
+
 struct PackArgs {
     const u32x4 *src[kMaxTensors];
     u32x4 *dst[kMaxTensors];
@@ -49,6 +68,18 @@ struct UnpackArgs {
     int B, N;
     int row_vec;
     Chunking ch;
+};
+
+struct RepackArgs {
+    const u32x4 *src[kMaxTensors];  // flat [>= T, row] (T = cu[B])
+    u32x4 *dst[kMaxTensors];        // flat [>= T2, row]
+    const uint8_t *keep2;           // [>= T], nonzero = keep the flat row
+    const int32_t *cu;              // [B+1] of src
+    int32_t *cu2;                   // [B+1] output
+    int32_t *total_out;             // nullable
+    int B;
+    int row_vec;                    // 16-byte vectors per row
+    int n_tensors;
 };
 
 enum class Elem { F32, F16, BF16 };
@@ -89,5 +120,6 @@ hipError_t launch_pack(const PackArgs &a, hipStream_t s);
 hipError_t launch_unpack(const UnpackArgs &a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s);
 hipError_t launch_fused(const FusedArgs &a, hipStream_t s);
+hipError_t launch_repack(const RepackArgs &a, hipStream_t s);
 
 }  // namespace rattn

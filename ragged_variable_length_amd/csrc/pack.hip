@@ -190,7 +190,7 @@ __device__ __forceinline__ int count_prefix_in_image(const uint8_t *keep_img, in
     return c;
 }
 
-template <bool kSelfScan>
+template <bool kSelfScan, int NT>
 __global__ __launch_bounds__(kPackThreads) void pack_kernel(PackArgs a) {
     __shared__ int list[64];
     __shared__ int red[kPackThreads / 64];
@@ -245,20 +245,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(PackArgs a) {
         const int e = idx - j * rv;
         const int64_t so = (img_row0 + list[j]) * rv + e;
         const int64_t d = (base + j) * rv + e;
-        const u32x4 x0 = a.src[0][so];
-        if (a.n_tensors == 1) {
-            a.dst[0][d] = x0;
-        } else if (a.n_tensors == 2) {
-            const u32x4 x1 = a.src[1][so];
-            a.dst[0][d] = x0;
-            a.dst[1][d] = x1;
-        } else {
-            const u32x4 x1 = a.src[1][so];
-            const u32x4 x2 = a.src[2][so];
-            a.dst[0][d] = x0;
-            a.dst[1][d] = x1;
-            a.dst[2][d] = x2;
-        }
+        copy_vec<NT>(a.src, a.dst, so, d);
     }
 }
 
@@ -302,19 +289,34 @@ __global__ __launch_bounds__(kPackThreads) void unpack_kernel(UnpackArgs a) {
 
 }  // namespace
 
-hipError_t launch_pack(const PackArgs &a, hipStream_t s) {
+namespace {
+
+template <int NT>
+hipError_t launch_pack_nt(const PackArgs &a, hipStream_t s) {
     const int64_t tokens = (int64_t)a.B * a.N;
     const int64_t wgs = (int64_t)a.B * a.ch.nchunks;
     if (tokens <= kSelfScanMaxTokens) {
-        hipLaunchKernelGGL(pack_kernel<true>, dim3((unsigned)(wgs + 1)), dim3(kPackThreads), 0, s, a);
+        hipLaunchKernelGGL((pack_kernel<true, NT>), dim3((unsigned)(wgs + 1)), dim3(kPackThreads),
+                           0, s, a);
         return hipGetLastError();
     }
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a.keep, a.B, a.N, a.cu,
                        a.max_out, a.total_out);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(pack_kernel<false>, dim3((unsigned)wgs), dim3(kPackThreads), 0, s, a);
+    hipLaunchKernelGGL((pack_kernel<false, NT>), dim3((unsigned)wgs), dim3(kPackThreads), 0, s, a);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_pack(const PackArgs &a, hipStream_t s) {
+    switch (a.n_tensors) {
+        case 1: return launch_pack_nt<1>(a, s);
+        case 2: return launch_pack_nt<2>(a, s);
+        case 3: return launch_pack_nt<3>(a, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_unpack(const UnpackArgs &a, hipStream_t s) {

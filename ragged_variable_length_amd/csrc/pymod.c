@@ -202,6 +202,47 @@ static PyObject *py_fused_padded(PyObject *self, PyObject *const *args, Py_ssize
                                               (float)scale, (rattn_dtype)dt, (void *)stream));
 }
 
+/* repack(srcs: sequence of int, dsts: sequence of int, keep2, cu_seqlens, B, row_elems, dtype,
+ *        cu_seqlens_out, total_out|None, stream) */
+static PyObject *py_repack(PyObject *self, PyObject *const *args, Py_ssize_t nargs) {
+    (void)self;
+    if (nargs_is(nargs, 10, "repack")) return NULL;
+    const void *src[RATTN_MAX_TENSORS] = {0}, *dst[RATTN_MAX_TENSORS] = {0};
+    PyObject *seqs[2] = {args[0], args[1]};
+    const void **outs[2] = {src, dst};
+    Py_ssize_t n = -1;
+    for (int s = 0; s < 2; ++s) {
+        PyObject *fast = PySequence_Fast(seqs[s], "repack: srcs and dsts must be sequences");
+        if (!fast) return NULL;
+        const Py_ssize_t len = PySequence_Fast_GET_SIZE(fast);
+        if (len < 1 || len > RATTN_MAX_TENSORS || (n >= 0 && len != n)) {
+            Py_DECREF(fast);
+            PyErr_SetString(PyExc_ValueError, "repack: 1-3 sources and as many destinations");
+            return NULL;
+        }
+        n = len;
+        for (Py_ssize_t i = 0; i < len; ++i) {
+            if (as_ptr(PySequence_Fast_GET_ITEM(fast, i), &outs[s][i])) {
+                Py_DECREF(fast);
+                return NULL;
+            }
+        }
+        Py_DECREF(fast);
+    }
+    PTR(2, keep2);
+    PTR(3, cu);
+    INT(4, B);
+    INT(5, row_elems);
+    INT(6, dt);
+    PTR(7, cu2);
+    PTR(8, tot);
+    PTR(9, stream);
+    return PyLong_FromLong(rattn_repack((const void *const *)src, (void *const *)dst, (int)n,
+                                        (const uint8_t *)keep2, (const int32_t *)cu, B, row_elems,
+                                        (rattn_dtype)dt, (int32_t *)cu2, (int32_t *)tot,
+                                        (void *)stream));
+}
+
 static PyMethodDef methods[] = {
     {"init", (PyCFunction)(void (*)(void))py_init, METH_FASTCALL, "rattn_init()"},
     {"status_string", (PyCFunction)(void (*)(void))py_status_string, METH_FASTCALL,
@@ -213,6 +254,7 @@ static PyMethodDef methods[] = {
     {"fused", (PyCFunction)(void (*)(void))py_fused, METH_FASTCALL, "rattn_fused(...)"},
     {"fused_padded", (PyCFunction)(void (*)(void))py_fused_padded, METH_FASTCALL,
      "rattn_fused_padded(...)"},
+    {"repack", (PyCFunction)(void (*)(void))py_repack, METH_FASTCALL, "rattn_repack(...)"},
     {NULL, NULL, 0, NULL}};
 
 static struct PyModuleDef module = {PyModuleDef_HEAD_INIT, "_rattn",

@@ -29,6 +29,7 @@
 #define __shared__ static
 typedef int hipError_t;
 #define hipSuccess 0
+#define hipErrorInvalidValue 1
 typedef void *hipStream_t;
 struct dim3 { unsigned x, y, z; dim3(unsigned a = 1, unsigned b = 1, unsigned c = 1) : x(a), y(b), z(c) {} };
 struct emu_idx { unsigned x, y, z; };

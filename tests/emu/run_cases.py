@@ -71,6 +71,11 @@ class CtypesBackend:
     def fused_padded(self, *a):
         return self.lib.rattn_fused_padded(*a)
 
+    def repack(self, srcs, dsts, *rest):
+        n = len(srcs)
+        P = self.c.c_void_p * n
+        return self.lib.rattn_repack(P(*srcs), P(*dsts), n, *rest)
+
 
 def three_call(w, max_seqlen=None):
     pipe = rv.RaggedPipeline(w.B, w.N, w.H, w.q.dtype, device="cpu")
@@ -162,6 +167,47 @@ def case_padded():
             assert np.array_equal(U.bits(cls), U.bits(ref_cls)), (w.name, pad, "cls")
         print(f"{w.name}: padded to {max(w.kept_counts)} and to {w.N}: bits equal to ragged",
               flush=True)
+
+
+def repack_check(flat, keep2, cu, n_tensors=1, name="repack"):
+    """rattn_repack on host tensors against the oracle: rows, cu_seqlens and
+    total bit-exact, rows past T2 untouched."""
+    T = int(cu[-1])
+    srcs = [flat] + [torch.roll(flat, i, 0).contiguous() for i in range(1, n_tensors)]
+    dsts = [torch.full_like(f, 7.0) for f in srcs]
+    k2 = torch.zeros(max(T, 1) + 16, dtype=torch.uint8)  # 16-byte multiple, padded tail
+    k2[:T] = keep2
+    cu_t = torch.from_numpy(np.asarray(cu, np.int32)).contiguous()
+    cu2 = torch.full_like(cu_t, -7)
+    tot = torch.full((1,), -7, dtype=torch.int32)
+    rv.rattn_repack(srcs, dsts, k2, cu_t, cu2, tot)
+    for s_, d_ in zip(srcs, dsts):
+        ref, ref_cu = oracle.repack(s_, keep2, cu)
+        T2 = ref.shape[0]
+        assert np.array_equal(U.bits(d_[:T2]), U.bits(ref)), (name, "rows")
+        assert (U.bits(d_[T2:]) == U.bits(torch.tensor(7.0, dtype=flat.dtype))).all(), (name, "tail")
+        assert cu2.numpy().tolist() == ref_cu.tolist(), (name, "cu")
+        assert int(tot) == T2, (name, "total")
+    print(f"{name}: T={T} -> T2={int(tot)} ({n_tensors} tensor(s)) bit-exact", flush=True)
+
+
+def case_repack():
+    g = torch.Generator().manual_seed(48)
+    # from a packed workload: ragged images, empty ones included
+    keep = _keep_lengths([1, 0, 17, 65, 300, 257, 0, 40], 320, seed=49)
+    w = workloads.custom(8, 320, 1, "bf16", keep=keep, seed=50, name="repack_src")
+    cu, _, T = oracle.scan(w.keep)
+    flat = torch.from_numpy(oracle.pack(w.q, w.keep).view(np.int16)).view(torch.bfloat16)
+    keep2 = (torch.rand(T, generator=g) < 0.5).to(torch.uint8)
+    repack_check(flat, keep2, cu, n_tensors=3, name="repack_bf16_x3")
+    repack_check(flat, torch.ones(T, dtype=torch.uint8), cu, name="repack_keep_all")
+    repack_check(flat, torch.zeros(T, dtype=torch.uint8), cu, name="repack_keep_none")
+    # fp32 rows, two tensors, a prefix count that is not a multiple of 16
+    w32 = workloads.custom(5, 37, 2, "f32", p_keep=0.7, seed=51, name="repack_f32")
+    cu32, _, T32 = oracle.scan(w32.keep)
+    flat32 = torch.from_numpy(oracle.pack(w32.q, w32.keep))
+    k32 = (torch.rand(T32, generator=g) < 0.3).to(torch.uint8)
+    repack_check(flat32, k32, cu32, n_tensors=2, name="repack_f32_x2")
 
 
 def case_long():

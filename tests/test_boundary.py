@@ -185,3 +185,16 @@ def test_padded_comparator_argument_checks(lib):
     # the fused checks apply too
     assert f(A, A, A, A, A, None, 2, 10, 2, 63, 5, ctypes.c_float(0.125), BF16, None) == UNSUPPORTED
     assert f(A, A, A, A, None, None, 2, 10, 2, 64, 5, ctypes.c_float(0.125), BF16, None) == INVALID
+
+
+def test_repack_argument_checks(lib):
+    P2 = ctypes.c_void_p * 1
+    src, dst = P2(A), P2(A + 0x1000)
+    f = lib.rattn_repack
+    assert f(src, dst, 1, A, A, 0, 128, BF16, A + 64, None, None) == OK      # B = 0: nothing
+    assert f(src, dst, 0, A, A, 2, 128, BF16, A + 64, None, None) == INVALID  # no tensors
+    assert f(src, dst, 4, A, A, 2, 128, BF16, A + 64, None, None) == INVALID  # too many
+    assert f(src, dst, 1, A + 1, A, 2, 128, BF16, A + 64, None, None) == INVALID  # keep2 misaligned
+    assert f(src, dst, 1, A, A, 2, 128, BF16, A, None, None) == INVALID       # cu_out aliases cu
+    assert f(src, P2(A), 1, A, A, 2, 128, BF16, A + 64, None, None) == INVALID  # dst == src
+    assert f(src, dst, 1, A, A, 2, 5, F32, A + 64, None, None) == INVALID     # row not 16 B

@@ -17,16 +17,14 @@ import workloads
 from tests._gpu_util import (FLAT_TOL, attention_error, bits, check_indexing, run_hip,
                              sample_rows, say)
 
-# The first GPU run of this module ended with the box reporting a GPU memory
-# fault or hung queue, with no output returned, so the failing test is unknown.
-# Every case here was then re-run on the CPU with the kernel sources compiled
-# for x86 (one thread per lane, real barriers, emulated wave intrinsics and
-# MFMA) under AddressSanitizer: all in bounds and all within tolerance, and no
-# mistake in the code was found.  Without a shown cause these cases stay off
-# the GPU; the same kernels are covered on the CPU by test_kernels_emulated.py.
-pytestmark = [pytest.mark.gpu, pytest.mark.skip(
-    reason="kept off the GPU: first run faulted the box, cause not found "
-           "(CPU emulation under ASan clean); see test_kernels_emulated.py")]
+# The first GPU run of this module faulted the GPU.  Cause: the pack kernel
+# branched at run time on the number of tensors it moves, and on the
+# three-tensor path the compiled code stored the second tensor's rows through
+# an SGPR pair that was never loaded with that tensor's address (the compiler
+# left it undefined).  Every test here packs q, k and v, so every one took that
+# path.  The copy kernels now take the tensor count as a template parameter;
+# tests/test_codegen.py checks the compiled stores on the CPU.
+pytestmark = pytest.mark.gpu
 
 
 @pytest.fixture(scope="module", autouse=True)

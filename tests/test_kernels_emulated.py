@@ -7,8 +7,9 @@ measured lane layouts) with AddressSanitizer, and driven through the Python
 binding and the C ABI on host tensors.  Every entry point is checked:
 rattn_pack, rattn_forward and rattn_unpack against the oracle (the scan and
 the row movement bit-exact, attention within the per-dtype tolerances of
-`_gpu_util`), rattn_fused bitwise against the three-call path, and
-rattn_fused_padded bitwise against rattn_fused.  Any out-of-bounds global or
+`_gpu_util`), rattn_fused bitwise against the three-call path,
+rattn_fused_padded bitwise against rattn_fused, and rattn_repack bit-exact
+against the oracle.  Any out-of-bounds global or
 LDS access aborts the run.
 
 These cases cover the three-call path, whose GPU parity tests are kept off the
@@ -46,7 +47,8 @@ def emu_lib(tmp_path_factory):
            "-I", os.path.join(HERE, "emu"), "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            "-x", "c++", os.path.join(HERE, "emu", "emu_runtime.cpp"),
            os.path.join(CSRC, "api.hip"), os.path.join(CSRC, "pack.hip"),
-           os.path.join(CSRC, "attention.hip"), "-o", out, "-lpthread"]
+           os.path.join(CSRC, "attention.hip"), os.path.join(CSRC, "repack.hip"), "-o", out,
+           "-lpthread"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-4000:]
     return out, rt
@@ -80,6 +82,10 @@ def test_emulated_long_sequences(emu_lib):
 
 def test_emulated_padded_comparator_matches_ragged(emu_lib):
     _run(emu_lib, "padded")
+
+
+def test_emulated_repack(emu_lib):
+    _run(emu_lib, "repack")
 
 
 def test_emulated_scan_over_single_launch_limit(emu_lib):
