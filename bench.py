@@ -37,7 +37,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 import workloads  # noqa: E402
-from ragged_variable_length_amd import FusedPlan, rattn_init  # noqa: E402
+from ragged_variable_length_amd import FusedPlan, RaggedPipeline, rattn_init  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, datasheet
 # HBM traffic of the fused kernel measured with rocprofv3 counters (FETCH_SIZE,
@@ -63,6 +63,23 @@ def fused_bytes(T: int, B: int, N: int, H: int, dtype: str) -> int:
 def attention_bytes(T: int, H: int, dtype: str) -> int:
     """the attention alone on a flat buffer: q, k, v read and o written once."""
     return 4 * T * H * 64 * ES[dtype]
+
+
+def three_call_bytes(T: int, B: int, N: int, H: int, dtype: str) -> int:
+    """rattn_pack (mask read, 3 kept rows read and written), rattn_forward
+    (attention_bytes) and rattn_unpack (mask read, T rows read, the padded
+    output and the CLS rows written)."""
+    row = H * 64 * ES[dtype]
+    pack = B * N + 2 * 3 * T * row
+    unpack = B * N + T * row + B * N * row + B * row
+    return pack + attention_bytes(T, H, dtype) + unpack
+
+
+def repack_bytes(T: int, T2: int, B: int, H: int, dtype: str) -> int:
+    """rattn_repack of q, k, v: the second keep flag of every row read, the
+    kept rows read and written once, both cu_seqlens."""
+    row = H * 64 * ES[dtype]
+    return T + 2 * 3 * T2 * row + 2 * 4 * (B + 1)
 
 
 def attention_flops(lengths, H: int) -> int:
@@ -177,11 +194,19 @@ class BenchStep(ctypes.Structure):
                 ("max_dev", ctypes.c_void_p), ("total_dev", ctypes.c_void_p),
                 ("B", ctypes.c_int), ("N", ctypes.c_int), ("H", ctypes.c_int),
                 ("max_seqlen", ctypes.c_int), ("dtype", ctypes.c_int), ("scale", ctypes.c_float),
-                ("stream", ctypes.c_void_p)]
+                ("stream", ctypes.c_void_p), ("layers", ctypes.c_int),
+                ("out_padded2", ctypes.c_void_p), ("keep2", ctypes.c_void_p),
+                ("cu2", ctypes.c_void_p), ("repacked", ctypes.c_void_p * 3)]
 
 
 WHAT_FORWARD = 0
+WHAT_THREE_CALL = 1
 WHAT_FUSED = 2
+WHAT_LAYERS_PACKED = 3
+WHAT_LAYERS_FUSED = 4
+WHAT_REPACK = 5
+REPACK_KEEP = 0.5   # fraction of the packed rows a second pruning stage keeps
+STACK_LAYERS = 12   # DeiT-S / DeiT-B depth
 _DT_CODE = {"f32": 0, "f16": 1, "bf16": 2}
 _timing = None
 
@@ -264,6 +289,96 @@ class FlatResident:
         return s
 
 
+class StackResident:
+    """A Resident plus the flat buffers of the three-call form (RaggedPipeline)
+    and a second padded buffer, for the three-call step and the layer stacks."""
+
+    def __init__(self, r: Resident, layers: int = STACK_LAYERS):
+        self.r = r
+        w = r.w
+        self.pipe = RaggedPipeline(w.B, w.N, w.H, r.q.dtype)
+        self.out2 = torch.empty_like(r.out)
+        self.layers = layers
+        g = torch.Generator().manual_seed(11)
+        cap = self.pipe.pq.shape[0]
+        self.keep2 = (torch.rand(cap, generator=g) < REPACK_KEEP).to(torch.uint8).to("cuda")
+        self.T2 = int(self.keep2[:r.T].sum().item())
+        self.cu2 = torch.empty_like(self.pipe.cu)
+        self.repacked = [torch.empty_like(self.pipe.pq) for _ in range(3)]
+        torch.cuda.synchronize()
+
+    def c_step(self) -> BenchStep:
+        s = self.r.c_step()
+        p = self.pipe
+        for i, t in enumerate((p.pq, p.pk, p.pv)):
+            s.packed[i] = t.data_ptr()
+        s.o, s.cu = p.po.data_ptr(), p.cu.data_ptr()
+        s.max_dev, s.total_dev = p.max_seqlen_dev.data_ptr(), p.total_dev.data_ptr()
+        s.layers, s.out_padded2 = self.layers, self.out2.data_ptr()
+        s.keep2, s.cu2 = self.keep2.data_ptr(), self.cu2.data_ptr()
+        for i, t in enumerate(self.repacked):
+            s.repacked[i] = t.data_ptr()
+        return s
+
+
+def c_region_us(step: BenchStep, what: int, reps: int, stream) -> float:
+    """Average device time of one `what` step: `reps` steps enqueued back to
+    back from C++, HIP events on the launch stream at the two ends only."""
+    lib = timing_lib()
+    if lib.bench_loop(ctypes.byref(step), what, 3) != 0:
+        raise RuntimeError(f"bench_loop({what}) failed")
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    if lib.bench_loop(ctypes.byref(step), what, reps) != 0:
+        raise RuntimeError(f"bench_loop({what}) failed")
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1000.0 / reps
+
+
+def three_call_and_stacks(r: Resident, reps: int) -> dict:
+    """The pages' three-call form (rattn_pack -> rattn_forward -> rattn_unpack)
+    against the one launch, and a stack of STACK_LAYERS attention layers on one
+    mask: packed once, attended per layer, unpacked once, against rattn_fused
+    per layer (integrated packing pipeline: the packed buffer is kept across
+    blocks).  Device time per step, warm, from back-to-back C++ enqueues."""
+    w = r.w
+    sr = StackResident(r)
+    cs = sr.c_step()
+    L = sr.layers
+    one = {w_: c_region_us(cs, w_, reps, r.stream) for w_ in (WHAT_THREE_CALL, WHAT_FUSED)}
+    stack_reps = max(1, reps // L)
+    packed = c_region_us(cs, WHAT_LAYERS_PACKED, stack_reps, r.stream)
+    fused = c_region_us(cs, WHAT_LAYERS_FUSED, stack_reps, r.stream)
+    tc_bytes = three_call_bytes(r.T, w.B, w.N, w.H, w.dtype)
+    c_region_us(cs, WHAT_THREE_CALL, 1, r.stream)  # the packed q, k, v the re-pack reads
+    rp = c_region_us(cs, WHAT_REPACK, reps, r.stream)
+    rp_bytes = repack_bytes(r.T, sr.T2, w.B, w.H, w.dtype)
+    return {
+        "three_call_us": round(one[WHAT_THREE_CALL], 2),
+        "three_call_bytes": tc_bytes,
+        "three_call_hbm_frac": round(tc_bytes / (one[WHAT_THREE_CALL] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "fused_us": round(one[WHAT_FUSED], 2),
+        "fused_speedup_vs_three_call": round(one[WHAT_THREE_CALL] / one[WHAT_FUSED], 3),
+        "stack": {
+            "layers": L,
+            "packed_once_us": round(packed, 2),
+            "packed_once_us_per_layer": round(packed / L, 2),
+            "fused_per_layer_us": round(fused, 2),
+            "fused_per_layer_us_per_layer": round(fused / L, 2),
+            "packed_speedup_vs_fused_per_layer": round(fused / packed, 3),
+            "packed_once_bytes": (three_call_bytes(r.T, w.B, w.N, w.H, w.dtype)
+                                  + (L - 1) * attention_bytes(r.T, w.H, w.dtype)),
+            "fused_per_layer_bytes": L * fused_bytes(r.T, w.B, w.N, w.H, w.dtype),
+        },
+        "repack": {"keep_fraction": REPACK_KEEP, "T": r.T, "T2": sr.T2, "tensors": 3,
+                   "us": round(rp, 2), "bytes": rp_bytes,
+                   "hbm_frac": round(rp_bytes / (rp * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+
+
 def dispatch_floors(stream, iters: int, warmup: int) -> dict:
     """Host call -> completion (C++ steady_clock) at serving batch sizes 1-4,
     80 % pruning, DeiT-B shape: the one-launch rattn_fused (also enqueue-only
@@ -288,6 +403,14 @@ def dispatch_floors(stream, iters: int, warmup: int) -> dict:
         row["fused_enqueue_us"] = st.as_dict()
         if lib.bench_graph_floor(ctypes.byref(cs), WHAT_FUSED, iters, warmup, ctypes.byref(st)) == 0:
             row["fused_graph_replay_sync_us"] = st.as_dict()
+        sr = StackResident(r)  # owns the flat buffers tc points into
+        tc = sr.c_step()
+        if lib.bench_call_floor(ctypes.byref(tc), WHAT_THREE_CALL, iters, warmup, ctypes.byref(st)):
+            raise RuntimeError("bench_call_floor (three-call) failed")
+        row["three_call_call_sync_us"] = st.as_dict()
+        if lib.bench_graph_floor(ctypes.byref(tc), WHAT_THREE_CALL, iters, warmup,
+                                 ctypes.byref(st)) == 0:
+            row["three_call_graph_replay_sync_us"] = st.as_dict()
         f = FlatResident(r.w, stream)
         if lib.bench_call_floor(ctypes.byref(f.c_step()), WHAT_FORWARD, iters, warmup,
                                 ctypes.byref(st)):
@@ -296,7 +419,8 @@ def dispatch_floors(stream, iters: int, warmup: int) -> dict:
         res[f"deit_b_B{B}_p80"] = row
         print(f"[bench] dispatch floor B={B}: fused call+sync {row['fused_call_sync_us']['median_us']} us,"
               f" enqueue {row['fused_enqueue_us']['median_us']} us, rattn_forward alone call+sync "
-              f"{row['forward_call_sync_us']['median_us']} us", flush=True)
+              f"{row['forward_call_sync_us']['median_us']} us, three calls + sync "
+              f"{row['three_call_call_sync_us']['median_us']} us", flush=True)
     return res
 
 
@@ -370,6 +494,7 @@ def large_configs(stream, launches: int) -> dict:
                "fused_bytes": nbytes, "attn_flops": flops,
                "traffic_bytes": measured_traffic(w.name)}
         row["padded_comparator"] = padded_comparison(r, launches)
+        row["three_call_and_stacks"] = three_call_and_stacks(r, launches)
         for cold in (False, True):
             us = kernel_time_us(r, launches, cold, flush)
             gbs = nbytes / (us * 1e-6) / 1e9
@@ -384,9 +509,22 @@ def large_configs(stream, launches: int) -> dict:
               f" cold {row['cold']['us']} us ({row['cold']['hbm_frac']:.3f}); padded comparator "
               f"{pc['padded_longest_us']} us (longest survivor) / {pc['padded_n_us']} us (N)",
               flush=True)
+        _print_stacks(name, row["three_call_and_stacks"])
         del r
     del flush
     return out
+
+
+STACK_WORKLOADS = {"deit_s_80pct": workloads.deit_s, "deit_b_384_50pct": workloads.deit_b_384,
+                   "large_batch_threshold_l2": workloads.large_batch}
+
+
+def _print_stacks(name: str, t: dict) -> None:
+    st = t["stack"]
+    print(f"[bench] {name}: three calls {t['three_call_us']} us vs one launch {t['fused_us']} us;"
+          f" {st['layers']} layers packed once {st['packed_once_us']} us vs rattn_fused per layer "
+          f"{st['fused_per_layer_us']} us ({st['packed_speedup_vs_fused_per_layer']}x); re-pack "
+          f"{t['repack']['us']} us ({t['repack']['hbm_frac']:.3f} of HBM)", flush=True)
 
 
 def cpu_baseline(w, budget_s: float) -> dict:
@@ -420,6 +558,9 @@ def main():
                     help="only the launches the traffic counters are read on, then exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the traffic summary of two counter runs, then exit")
+    ap.add_argument("--stack-only", choices=sorted(STACK_WORKLOADS),
+                    help="only the three-call step, the layer stacks and the re-pack of one "
+                         "workload (for a kernel trace of those kernels), then exit")
     args = ap.parse_args()
     if args.pmc_summary:
         sys.stdout.write(summarize_pmc(*args.pmc_summary))
@@ -434,6 +575,14 @@ def main():
         sys.exit(1)
     if args.pmc_target:
         pmc_target()
+        return
+    if args.stack_only:
+        rattn_init()
+        stream = torch.cuda.current_stream()
+        w = STACK_WORKLOADS[args.stack_only]()
+        t = three_call_and_stacks(Resident(w, stream), 200)
+        _print_stacks(w.name, t)
+        print(json.dumps({"workload": w.name, "three_call_and_stacks": t}), flush=True)
         return
     rattn_init()
     stream = torch.cuda.current_stream()
@@ -488,6 +637,8 @@ def main():
         pc = line["padded_comparator"]
         print(f"[bench] {w.name}: ragged {pc['ragged_us']} us, padded to longest survivor "
               f"{pc['padded_longest_us']} us, padded to N {pc['padded_n_us']} us", flush=True)
+        line["three_call_and_stacks"] = three_call_and_stacks(r, 500)
+        _print_stacks(w.name, line["three_call_and_stacks"])
         side = torch.cuda.Stream()  # graph capture needs a non-default stream
         line["dispatch_floor"] = dispatch_floors(side, iters=1000, warmup=100)
         line["large_configs"] = large_configs(stream, launches=50)

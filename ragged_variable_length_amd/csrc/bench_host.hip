@@ -10,10 +10,15 @@
 //   * rattn_forward + sync, the whole pack -> forward -> unpack step + sync, and
 //     the one-launch rattn_fused + sync;
 //   * the same step replayed from a captured hipGraph + sync;
-//   * enqueue-only cost of the calls (no sync inside the timed span).
+//   * enqueue-only cost of the calls (no sync inside the timed span);
+//   * a stack of attention layers on one keep mask: packed once, attended per
+//     layer, unpacked once (section on the integrated packing pipeline: the
+//     packed buffer is kept across blocks), against the one-launch form
+//     repeated per layer.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <utility>
 #include <chrono>
 #include <vector>
 
@@ -38,6 +43,11 @@ typedef struct bench_step {
     int B, N, H, max_seqlen, dtype;
     float scale;
     void *stream;
+    int layers;           // attention layers of the stacked steps (what = 3, 4)
+    void *out_padded2;    // second padded [B, N, H, 64] buffer for the stacked one-launch form
+    const uint8_t *keep2; // [>= T] second keep flag per flat row (what = 5)
+    int32_t *cu2;         // [B+1] cu_seqlens after the re-pack
+    void *repacked[3];    // flat q, k, v after the re-pack [>= T2, H, 64]
 } bench_step;
 
 }  // extern "C"
@@ -83,10 +93,64 @@ rattn_status do_fused(const bench_step *a) {
                        a->stream);
 }
 
+// `layers` attention layers on one mask, each layer's output the next layer's
+// query (k and v stay those of the first layer: the work per layer is the same
+// as with fresh k, v): rattn_pack once, rattn_forward per layer on the flat
+// buffers (ping-pong between the flat q and o), rattn_unpack of the last
+// output once.
+rattn_status do_layers_packed(const bench_step *a) {
+    const int row = a->H * RATTN_HEAD_DIM;
+    const rattn_dtype dt = (rattn_dtype)a->dtype;
+    rattn_status s = rattn_pack(a->src, a->packed, 3, a->keep, a->B, a->N, row, dt, a->cu,
+                                a->max_dev, a->total_dev, a->stream);
+    void *qb = a->packed[0], *ob = a->o;
+    for (int l = 0; s == RATTN_OK && l < a->layers; ++l) {
+        s = rattn_forward(qb, a->packed[1], a->packed[2], ob, a->cu, a->B, a->max_seqlen, a->H,
+                          RATTN_HEAD_DIM, a->scale, dt, a->stream);
+        std::swap(qb, ob);
+    }
+    if (s != RATTN_OK) return s;
+    return rattn_unpack(qb, a->out_padded, a->cls, a->keep, a->cu, a->B, a->N, row, dt, a->stream);
+}
+
+// The same stack with the one-launch form per layer: every layer gathers from
+// and scatters to the padded layout (ping-pong between out_padded and
+// out_padded2); the CLS rows are written by the last layer.
+rattn_status do_layers_fused(const bench_step *a) {
+    const void *qb = a->src[0];
+    void *ob = a->out_padded, *other = a->out_padded2;
+    rattn_status s = RATTN_OK;
+    for (int l = 0; s == RATTN_OK && l < a->layers; ++l) {
+        s = rattn_fused(qb, a->src[1], a->src[2], a->keep, ob, l == a->layers - 1 ? a->cls : nullptr,
+                        a->B, a->N, a->H, RATTN_HEAD_DIM, a->max_seqlen, a->scale,
+                        (rattn_dtype)a->dtype, a->stream);
+        qb = ob;
+        std::swap(ob, other);
+    }
+    return s;
+}
+
+// A later pruning stage on the packed q, k, v (which a preceding what = 1 or 3
+// step has written): rattn_repack under keep2.
+rattn_status do_repack(const bench_step *a) {
+    return rattn_repack(a->packed, a->repacked, 3, a->keep2, a->cu, a->B, a->H * RATTN_HEAD_DIM,
+                        (rattn_dtype)a->dtype, a->cu2, nullptr, a->stream);
+}
+
 // what = 0: rattn_forward; 1: rattn_pack + rattn_forward + rattn_unpack;
-// 2: rattn_fused (the same pack -> attend -> unpack in one launch).
+// 2: rattn_fused (the same pack -> attend -> unpack in one launch);
+// 3: `layers` layers packed once (do_layers_packed); 4: the same layers with
+// rattn_fused per layer (do_layers_fused); 5: rattn_repack (do_repack).
 rattn_status run(const bench_step *a, int what) {
-    return what == 0 ? do_forward(a) : what == 1 ? do_step(a) : do_fused(a);
+    switch (what) {
+        case 0: return do_forward(a);
+        case 1: return do_step(a);
+        case 2: return do_fused(a);
+        case 3: return do_layers_packed(a);
+        case 4: return do_layers_fused(a);
+        case 5: return do_repack(a);
+        default: return RATTN_ERR_INVALID_ARG;
+    }
 }
 
 }  // namespace
