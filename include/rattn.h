@@ -175,8 +175,9 @@ rattn_status rattn_unpack(const void *src, void *dst_padded, void *cls,
  *               the attention output, pruned positions all-zero bytes
  *   cls         device, [B, H, head_dim] (nullable): row (b, 0) of that
  *               output (zeros when the CLS token was pruned)
- *   B, N, H     B >= 0, 1 <= N <= RATTN_MAX_FUSED_N, H >= 1, and
- *               N * H * head_dim * element size <= RATTN_MAX_IMAGE_BYTES
+ *   B, N, H     B >= 0, 1 <= N <= RATTN_MAX_FUSED_N, 1 <= H, H * head_dim
+ *               < 2^24, and N * H * head_dim * element size <=
+ *               RATTN_MAX_IMAGE_BYTES
  *   head_dim    must be RATTN_HEAD_DIM
  *   max_seqlen  host upper bound on every kept count (N is always valid)
  *   scale, dt   as for rattn_forward

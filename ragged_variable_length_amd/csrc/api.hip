@@ -210,7 +210,9 @@ rattn_status fused_common(const void *q, const void *k, const void *v, const uin
     if (elem_size(dt) == 0) return RATTN_ERR_INVALID_ARG;
     if (B < 0 || N < 1 || H < 1 || max_seqlen < 0 || !std::isfinite(scale))
         return RATTN_ERR_INVALID_ARG;
-    if ((int64_t)B * N > RATTN_MAX_TOKENS || (int64_t)H * RATTN_HEAD_DIM > (1 << 24))
+    // row strides below 2^24 elements: the kernels form padded row offsets
+    // with a 24-bit multiply
+    if ((int64_t)B * N > RATTN_MAX_TOKENS || (int64_t)H * RATTN_HEAD_DIM >= (1 << 24))
         return RATTN_ERR_INVALID_ARG;
     if (head_dim != RATTN_HEAD_DIM || N > RATTN_MAX_FUSED_N) return RATTN_ERR_UNSUPPORTED;
     if ((int64_t)N * H * head_dim * elem_size(dt) > RATTN_MAX_IMAGE_BYTES) return RATTN_ERR_UNSUPPORTED;

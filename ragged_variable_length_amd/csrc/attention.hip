@@ -129,7 +129,9 @@ struct FlatRows {
 struct PaddedRows {
     uint32_t rs;
     const int16_t *pos;  // LDS: position of the r-th kept token
-    __device__ __forceinline__ uint32_t off(int r) const { return (uint32_t)pos[r] * rs; }
+    // full-rate 24-bit multiply: pos < 2^11 and rs < 2^24, and the host keeps
+    // one image's rows under 2^31 bytes, so the product fits 32 bits
+    __device__ __forceinline__ uint32_t off(int r) const { return __umul24((uint32_t)pos[r], rs); }
 };
 
 // LDS tiles of the 16-bit path are 64 rows x 128 bytes, written by
@@ -203,17 +205,23 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
     constexpr int kDmaPerWave = 16 / W;
     const int srow = lane >> 3, sslot = lane & 7;
     auto stage = [&](int chunk, int buf) {
+        // the row offsets of all of this wavefront's copies first (in the
+        // padded layout they are LDS reads), then the copies
+        uint32_t ro[kDmaPerWave];
 #pragma unroll
         for (int i = 0; i < kDmaPerWave; ++i) {
             const int idx = wid * kDmaPerWave + i;  // 0..7: K blocks, 8..15: V blocks
+            ro[i] = R.off(min(chunk * kKC + 8 * (idx & 7) + srow, L - 1));
+        }
+#pragma unroll
+        for (int i = 0; i < kDmaPerWave; ++i) {
+            const int idx = wid * kDmaPerWave + i;
             const bool is_v = idx >= 8;
             const int row0 = 8 * (idx & 7);
             const int row = row0 + srow;
-            const int key = min(chunk * kKC + row, L - 1);
             uint16_t *dst = (is_v ? sV : sK) + buf * (kKC * 64) + row0 * 64;
-            const uint32_t ro = R.off(key);
-            const uint16_t *src = is_v ? vh + ro + 8 * vpiece(row, sslot)
-                                       : kh + ro + 8 * kpiece(row, sslot);
+            const uint16_t *src = is_v ? vh + ro[i] + 8 * vpiece(row, sslot)
+                                       : kh + ro[i] + 8 * kpiece(row, sslot);
             __builtin_amdgcn_global_load_lds(src, RATTN_LDS(dst), 16, 0, 0);
         }
     };

@@ -73,6 +73,7 @@ inline uint64_t __ballot(int pred) {
 }
 inline int __popc(uint32_t x) { return __builtin_popcount(x); }
 inline int __popcll(uint64_t x) { return __builtin_popcountll(x); }
+inline unsigned __umul24(unsigned a, unsigned b) { return (a & 0xFFFFFFu) * (b & 0xFFFFFFu); }
 inline int atomicAdd(int *p, int v) { return __atomic_fetch_add(p, v, __ATOMIC_SEQ_CST); }
 
 typedef float emu_f32x4 __attribute__((ext_vector_type(4)));

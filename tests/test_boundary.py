@@ -187,6 +187,19 @@ def test_padded_comparator_argument_checks(lib):
     assert f(A, A, A, A, None, None, 2, 10, 2, 64, 5, ctypes.c_float(0.125), BF16, None) == INVALID
 
 
+def test_fused_row_stride_limit(lib):
+    """Row strides (H * head_dim elements) must stay below 2^24: the fused
+    kernels form padded row offsets with a 24-bit multiply."""
+    H = (1 << 24) // 64
+    for f, last in ((lib.rattn_fused, 1), (lib.rattn_fused_padded, 1)):
+        assert f(A, A, A, A, A, None, 1, 1, H, 64, last, ctypes.c_float(0.125), BF16,
+                 None) == INVALID
+    # one head less passes the checks and reaches the device query
+    st = lib.rattn_fused(A, A, A, A, A, None, 1, 1, H - 1, 64, 1, ctypes.c_float(0.125), BF16,
+                         None)
+    assert st not in (INVALID, UNSUPPORTED)
+
+
 def test_repack_argument_checks(lib):
     P2 = ctypes.c_void_p * 1
     src, dst = P2(A), P2(A + 0x1000)
