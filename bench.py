@@ -464,6 +464,38 @@ def kernel_time_us(r: Resident, launches: int, cold: bool, flush_buf=None) -> fl
     return times[len(times) // 2]
 
 
+def forward_alone(w, stream, launches: int, flush_buf) -> dict:
+    """rattn_forward alone on the flat buffers of a workload (prepared on the
+    host, resident in HBM), against its own algorithmic bytes (q, k, v read and
+    o written once): warm, back-to-back region average from C++; cold, median
+    of single launches between HIP events, each after a 512 MB write that
+    evicts the MALL."""
+    f = FlatResident(w, stream)
+    step = f.c_step()
+    lib = timing_lib()
+    warm = c_region_us(step, WHAT_FORWARD, launches, stream)
+    times = []
+    for _ in range(launches):
+        flush_buf.zero_()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        if lib.bench_loop(ctypes.byref(step), WHAT_FORWARD, 1) != 0:
+            raise RuntimeError("bench_loop(forward) failed")
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) * 1000.0)
+    times.sort()
+    cold = times[len(times) // 2]
+    T = int(f.cu[-1].item())
+    nbytes = attention_bytes(T, w.H, w.dtype)
+    out = {"bytes": nbytes}
+    for name, us in (("warm", warm), ("cold", cold)):
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[name] = {"us": round(us, 2), "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    return out
+
+
 def padded_comparison(r: Resident, launches: int) -> dict:
     """The ragged kernel against its dense comparator (rattn_fused_padded,
     same outputs): every image padded to the longest survivor, and to N (no
@@ -495,6 +527,7 @@ def large_configs(stream, launches: int) -> dict:
                "traffic_bytes": measured_traffic(w.name)}
         row["padded_comparator"] = padded_comparison(r, launches)
         row["three_call_and_stacks"] = three_call_and_stacks(r, launches)
+        row["forward_alone"] = forward_alone(w, stream, launches, flush)
         for cold in (False, True):
             us = kernel_time_us(r, launches, cold, flush)
             gbs = nbytes / (us * 1e-6) / 1e9
@@ -510,6 +543,10 @@ def large_configs(stream, launches: int) -> dict:
               f"{pc['padded_longest_us']} us (longest survivor) / {pc['padded_n_us']} us (N)",
               flush=True)
         _print_stacks(name, row["three_call_and_stacks"])
+        fa = row["forward_alone"]
+        print(f"[bench] {name}: rattn_forward alone warm {fa['warm']['us']} us "
+              f"({fa['warm']['hbm_frac']:.3f} of HBM), cold {fa['cold']['us']} us "
+              f"({fa['cold']['hbm_frac']:.3f})", flush=True)
         del r
     del flush
     return out

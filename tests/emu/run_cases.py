@@ -211,11 +211,15 @@ def case_repack():
 
 
 def case_long():
-    # longer than 256 positions: 16-wavefront workgroups, two 256-row query
-    # tiles, five 64-key chunks streamed through the double buffer
+    # longer than 256 positions: 4x2 workgroups (128-row query tiles), five
+    # 64-key chunks streamed through the double buffer
     check_both(workloads.custom(2, 300, 1, "bf16", p_keep=0.95, seed=44, name="long_300_bf16"),
                flat=False)
     check_both(workloads.custom(1, 300, 1, "f16", p_keep=0.9, seed=45, name="long_300_f16"),
+               flat=False)
+    # two, three and four chunks per image
+    keep = _keep_lengths([100, 150, 200], 300, seed=52)
+    check_both(workloads.custom(3, 300, 1, "bf16", keep=keep, seed=53, name="long_chunks_2_3_4"),
                flat=False)
 
 
