@@ -28,8 +28,8 @@ namespace {
 
 constexpr int kPackThreads = 256;
 constexpr int kScanThreads = 1024;
-constexpr int kScanTileBig = 8192;    // image counts per LDS tile, 1024-thread scan
-constexpr int kScanTileSmall = 2048;  // same, 256-thread scan inside the pack launch
+constexpr int kScanWordsBig = 8;    // 16-byte mask words per thread and round, 1024-thread scan
+constexpr int kScanWordsSmall = 4;  // same, 256-thread scan inside the pack launch
 
 __device__ __forceinline__ int nonzero_bytes(uint32_t w) {
     // bit 7 of each byte of t is set iff that byte of w is nonzero
@@ -100,71 +100,114 @@ __device__ __forceinline__ u32x4 load_mask_word(const uint8_t *keep, int64_t w, 
     return r;
 }
 
-// cu_seqlens[0..B], max kept count and total, computed by one workgroup.
-// Per-image counts of a tile of images are accumulated in LDS from 16-byte
-// words of the flat mask (a word may straddle image boundaries), then scanned.
-template <int NT, int TILE>
-__device__ void scan_images(const uint8_t *keep, int B, int N, int32_t *cu, int32_t *max_out,
-                            int32_t *total_out, int *cnt, int *red) {
+// The nonzero bytes of a 16-byte mask word as 16 flag bits of one 32-bit
+// word: byte i of dword d sets bit 8*i + 7 - d.  (Bit 7 of each byte of
+// ((w & 0x7F7F7F7F) + 0x7F7F7F7F) | w is set iff that byte of w is nonzero;
+// the four dwords' flags are then interleaved by shifting dword d right d.)
+__device__ __forceinline__ uint32_t nonzero_flags(u32x4 x) {
+    uint32_t r = 0;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+        r |= ((((x[d] & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x[d]) & 0x80808080u) >> d;
+    return r;
+}
+
+// The flag bits of nonzero_flags for bytes 0 .. k-1 of the word (k < 16):
+// dwords d < k/4 whole, then the first k%4 bytes of dword k/4.
+__device__ __forceinline__ uint32_t flags_below(int k) {
+    const int D = k >> 2, rb = k & 3;
+    const uint32_t whole = ((0xFF00u >> D) & 0xFFu) * 0x01010101u;
+    const uint32_t part = ((1u << (8 * rb)) - 1u) & (0x80808080u >> D);
+    return whole | part;
+}
+
+// cu_seqlens[0..B], max kept count and total, computed by one workgroup of NT
+// threads.  The flat [B*N] mask is read as 16-byte words, WPT consecutive
+// words per thread and NT*WPT words per round, all of a thread's loads issued
+// before the first is used.  Each word's nonzero flags go to LDS (`flg`), and
+// one block scan of the per-thread counts gives every word's exclusive prefix
+// (`pre`).  The kept count before byte e is then
+// pre[e/16] + popcount(flg[e/16] & flags_below(e%16)): cu[b] is that value at
+// e = b*N, wherever the image boundary falls inside a word.  An image's kept
+// count is the difference of its two boundary values; one whose boundaries
+// lie in different rounds takes its first value from the previous round
+// (`carry_v`).  No atomics, no per-byte loop, no second pass over the mask.
+template <int NT, int WPT>
+__device__ __forceinline__ void scan_images(const uint8_t *keep, int B, int N, int32_t *cu,
+                                            int32_t *max_out, int32_t *total_out, int *pre,
+                                            uint32_t *flg, int *red) {
+    constexpr int TW = NT * WPT;
+    __shared__ int carry_v, last_b;  // value and index of the last boundary computed
     const int tid = threadIdx.x;
     const int64_t nbytes = (int64_t)B * N;
-    int carry = 0, mx = 0;
-    if (tid == 0) cu[0] = 0;
-    for (int b0 = 0; b0 < B; b0 += TILE) {
-        const int nb = min(TILE, B - b0);
-        for (int i = tid; i < nb; i += NT) cnt[i] = 0;
-        __syncthreads();
-        const int64_t lo = (int64_t)b0 * N, hi = (int64_t)(b0 + nb) * N;
-        for (int64_t w = (lo >> 4) + tid; w < (hi + 15) >> 4; w += NT) {
-            const u32x4 x = load_mask_word(keep, w, nbytes);
-            int64_t pos = w * 16;
-            int img = (int)(pos / N);
-            int64_t bound = (int64_t)(img + 1) * N;
-            int c = 0;
+    const int64_t nwords = (nbytes + 15) >> 4;
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    if (tid == 0) last_b = -1;
+    __syncthreads();
+    int carry = 0, m = 0;
+    for (int64_t w0 = 0; w0 < nwords; w0 += TW) {
+        // the previous round's last boundary, read before this round's first
+        // barrier (it is rewritten only after that)
+        const int prev_v = carry_v, prev_b = last_b;
+        const int64_t wt = w0 + (int64_t)tid * WPT;
+        u32x4 x[WPT];
 #pragma unroll
-            for (int j = 0; j < 16; ++j, ++pos) {
-                if (pos >= bound) {
-                    if (c) atomicAdd(&cnt[img - b0], c);
-                    c = 0;
-                    ++img;
-                    bound += N;
-                }
-                const uint32_t byte = (x[j >> 2] >> (8 * (j & 3))) & 0xFFu;
-                if (pos >= lo && pos < hi) c += byte != 0u;
-            }
-            if (c) atomicAdd(&cnt[img - b0], c);
+        for (int j = 0; j < WPT; ++j) x[j] = wt + j < nwords ? load_mask_word(keep, wt + j, nbytes) : zero4;
+        uint32_t fl[WPT];
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j < WPT; ++j) {
+            fl[j] = nonzero_flags(x[j]);
+            c += __popc(fl[j]);
+        }
+        int round_total;
+        int run = block_exclusive_scan<NT>(c, red, &round_total);
+#pragma unroll
+        for (int j = 0; j < WPT; ++j) {
+            pre[tid * WPT + j] = run;
+            flg[tid * WPT + j] = fl[j];
+            run += __popc(fl[j]);
         }
         __syncthreads();
-        // each thread scans a contiguous segment of the tile's counts
-        const int seg = (nb + NT - 1) / NT;
-        const int i0 = min(nb, tid * seg), i1 = min(nb, i0 + seg);
-        int s = 0, m = 0;
-        for (int i = i0; i < i1; ++i) {
-            s += cnt[i];
-            m = max(m, cnt[i]);
+        // kept count before byte e, for e inside this round's words
+        const int64_t lo = w0 * 16, hi = min(w0 + TW, nwords) * 16;
+        auto value_at = [&](int64_t e) {
+            const int i = (int)((e >> 4) - w0);
+            return carry + pre[i] + __popc(flg[i] & flags_below((int)(e & 15)));
+        };
+        // images whose first byte b*N lies in this round's words
+        const int64_t b0 = (lo + N - 1) / N;
+        const int64_t b_end = min((int64_t)B + 1, (hi + N - 1) / N);
+        for (int64_t b = b0 + tid; b < b_end; b += NT) {
+            const int v = value_at(b * N);
+            cu[b] = v;
+            if (b < B && (b + 1) * N < hi) m = max(m, value_at((b + 1) * N) - v);
+            if (b == b0 && b > 0 && prev_b == b - 1) m = max(m, v - prev_v);  // image b-1 began earlier
+            if (b == b_end - 1) {
+                carry_v = v;
+                last_b = (int)b;
+            }
         }
-        int tile_total;
-        int run = carry + block_exclusive_scan<NT>(s, red, &tile_total);
-        for (int i = i0; i < i1; ++i) {
-            run += cnt[i];
-            cu[b0 + i + 1] = run;
-        }
-        mx = max(mx, block_max<NT>(m, red));
-        carry += tile_total;
-        __syncthreads();  // cnt is reused by the next tile
+        carry += round_total;
+        __syncthreads();  // pre, flg and the carried boundary are rewritten next round
     }
     if (tid == 0) {
-        if (max_out) *max_out = mx;
+        cu[0] = 0;
+        cu[B] = carry;  // also when B*N is a multiple of 16 (no word holds byte B*N)
         if (total_out) *total_out = carry;
+        if (B > 0 && last_b == B - 1) m = max(m, carry - carry_v);  // the last image ends at byte B*N
     }
+    m = block_max<NT>(m, red);
+    if (tid == 0 && max_out) *max_out = m;
 }
 
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(const uint8_t *keep, int B, int N,
                                                             int32_t *cu, int32_t *max_out,
                                                             int32_t *total_out) {
-    __shared__ int cnt[kScanTileBig];
+    __shared__ int pre[kScanThreads * kScanWordsBig];
+    __shared__ uint32_t flg[kScanThreads * kScanWordsBig];
     __shared__ int red[kScanThreads / 64];
-    scan_images<kScanThreads, kScanTileBig>(keep, B, N, cu, max_out, total_out, cnt, red);
+    scan_images<kScanThreads, kScanWordsBig>(keep, B, N, cu, max_out, total_out, pre, flg, red);
 }
 
 // Rank the kept tokens of positions [cs, ce) of image b with one ballot.
@@ -199,9 +242,10 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(PackArgs a) {
     int wg = blockIdx.x;
     if constexpr (kSelfScan) {
         if (wg == 0) {
-            __shared__ int cnt[kScanTileSmall];
-            scan_images<kPackThreads, kScanTileSmall>(a.keep, a.B, a.N, a.cu, a.max_out,
-                                                      a.total_out, cnt, red);
+            __shared__ int pre[kPackThreads * kScanWordsSmall];
+            __shared__ uint32_t flg[kPackThreads * kScanWordsSmall];
+            scan_images<kPackThreads, kScanWordsSmall>(a.keep, a.B, a.N, a.cu, a.max_out,
+                                                       a.total_out, pre, flg, red);
             return;
         }
         wg -= 1;

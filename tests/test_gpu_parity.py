@@ -163,6 +163,35 @@ def test_scan_shapes(B, N):
     _full_check(w, flat=False)
 
 
+@pytest.mark.parametrize("B,N", [(1024, 16), (1100, 16), (9000, 1), (700, 197), (1, 20000),
+                                 (3, 50001)])
+def test_scan_and_pack_only_shapes(B, N):
+    """cu_seqlens, max, total and the packed rows, bit-exact, at mask shapes
+    the attention check would make slow: B*N exactly at and just above the
+    single-launch limit with every image boundary on a 16-byte word boundary,
+    sixteen boundaries per word, two rounds of the scan workgroup, and single
+    images longer than the limit."""
+    import ragged_variable_length_amd as rv
+    say(f"scan+pack B={B} N={N}")
+    g = torch.Generator().manual_seed(B + N)
+    keep = (torch.rand(B, N, generator=g) < 0.6).to(torch.uint8)
+    keep[:, 0] = 1
+    src = torch.randn(B, N, 8, generator=g).to(torch.bfloat16)  # 16-byte rows
+    dev = torch.device("cuda")
+    cu_ref, mx_ref, T = oracle.scan(keep)
+    dst = torch.full((B * N, 8), 7.0, dtype=torch.bfloat16, device=dev)
+    cu = torch.full((B + 1,), -7, dtype=torch.int32, device=dev)
+    mx = torch.full((1,), -7, dtype=torch.int32, device=dev)
+    tot = torch.full((1,), -7, dtype=torch.int32, device=dev)
+    rv.rattn_pack([src.to(dev)], [dst], keep.to(dev), cu, mx, tot)
+    torch.cuda.synchronize()
+    assert cu.cpu().numpy().tolist() == cu_ref.tolist(), "cu_seqlens"
+    assert int(mx.item()) == mx_ref and int(tot.item()) == T, "max / total"
+    d = dst.cpu()
+    assert np.array_equal(bits(d[:T]), bits(oracle.pack(src, keep))), "packed rows"
+    assert np.all(bits(d[T:]) == bits(torch.tensor(7.0, dtype=torch.bfloat16))), "rows past T"
+
+
 def test_max_seqlen_bound_does_not_change_bits():
     w = workloads.deit_s()
     exact = max(w.kept_counts)
