@@ -1,5 +1,6 @@
 // internal.h -- kernel launch descriptors shared by the library's translation
-// units (api.hip calls the launchers defined in pack.hip and attention.hip).
+// units (api.hip calls the launchers defined in pack.hip, attention.hip and
+// repack.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -80,6 +81,7 @@ struct RepackArgs {
     int B;
     int row_vec;                    // 16-byte vectors per row
     int n_tensors;
+    int slices;                     // workgroups per image (set by the launcher)
 };
 
 enum class Elem { F32, F16, BF16 };

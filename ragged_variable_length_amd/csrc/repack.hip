@@ -8,13 +8,18 @@
 // prune again at later blocks.  Re-packing keeps the buffer ragged from one
 // stage to the next instead of going back through the padded layout.
 //
-// Design on CDNA4: one workgroup per image.  The workgroup counts the kept
-// flags of all rows before its image itself (16-byte loads, SWAR byte
-// popcount, one block reduction), so the whole re-pack is ONE launch with no
+// Design on CDNA4: each image's rows are split into `slices` contiguous
+// slices, one workgroup each (the host picks the count from B alone so that
+// small batches still fill the chip).  A workgroup counts the kept flags of
+// all rows before its slice itself (16-byte loads, SWAR byte popcount, one
+// block reduction), so the whole re-pack is ONE launch with no
 // inter-workgroup communication.  Its own rows are ranked 256 at a time with
 // one wavefront ballot per 64 rows; the kept rows then move as 16-byte
 // vectors, lanes of the workgroup covering consecutive pieces of consecutive
-// rows.
+// rows.  The last slice of an image writes that image's new cu_seqlens
+// entry.
+#include <algorithm>
+
 #include "internal.h"
 
 namespace rattn {
@@ -34,9 +39,11 @@ __global__ __launch_bounds__(kRepackThreads) void repack_kernel(RepackArgs a) {
     __shared__ int red[kRepackWaves];
     __shared__ int wave_cnt[kRepackWaves];
     __shared__ int list[kRepackThreads];
-    const int b = blockIdx.x;
+    const int b = blockIdx.x / a.slices, slice = blockIdx.x - b * a.slices;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int s = a.cu[b], e = a.cu[b + 1];
+    const int img0 = a.cu[b], len = a.cu[b + 1] - img0;
+    const int s = img0 + (int)((int64_t)len * slice / a.slices);
+    const int e = img0 + (int)((int64_t)len * (slice + 1) / a.slices);
 
     // kept flags of rows [0, s): whole 16-byte words, then the tail bytes
     int c = 0;
@@ -84,7 +91,7 @@ __global__ __launch_bounds__(kRepackThreads) void repack_kernel(RepackArgs a) {
         carry += total;
         __syncthreads();  // list and wave_cnt are rewritten by the next round
     }
-    if (tid == 0) {
+    if (tid == 0 && slice == a.slices - 1) {
         if (b == 0) a.cu2[0] = 0;
         a.cu2[b + 1] = base + carry;
         if (a.total_out && b == a.B - 1) *a.total_out = base + carry;
@@ -93,8 +100,11 @@ __global__ __launch_bounds__(kRepackThreads) void repack_kernel(RepackArgs a) {
 
 }  // namespace
 
-hipError_t launch_repack(const RepackArgs &a, hipStream_t s) {
-    const dim3 grid((unsigned)a.B), block(kRepackThreads);
+hipError_t launch_repack(const RepackArgs &args, hipStream_t s) {
+    // about 512 workgroups whatever the batch: up to 16 slices per image
+    RepackArgs a = args;
+    a.slices = (int)std::min<int64_t>(16, std::max<int64_t>(1, (512 + (int64_t)a.B - 1) / a.B));
+    const dim3 grid((unsigned)((int64_t)a.B * a.slices)), block(kRepackThreads);
     switch (a.n_tensors) {
         case 1: hipLaunchKernelGGL(repack_kernel<1>, grid, block, 0, s, a); break;
         case 2: hipLaunchKernelGGL(repack_kernel<2>, grid, block, 0, s, a); break;
