@@ -28,23 +28,46 @@ inline Chunking chunking_for(int N) {
     return c;
 }
 
-// Moves 16-byte vector `so` of each of NT source tensors to vector `d` of the
-// matching destination.  The tensor count is a compile-time constant on
-// purpose: behind a run-time branch on the count (1, 2 or 3 tensors), the
-// gfx950 code generator of ROCm 7.2 structurized the three cases so that on
-// the three-tensor path the register holding the second destination's base
-// address was never written, and that store went to an unrelated address.
-// Straight-line code per count has no such join.
-template <int NT>
-__device__ __forceinline__ void copy_vec(const u32x4 *const (&src)[kMaxTensors],
-                                         u32x4 *const (&dst)[kMaxTensors], int64_t so,
-                                         int64_t d) {
+// Moves `total` 16-byte vector slots of NT tensors with a workgroup of
+// NThreads threads: slot idx goes from vector so of each source tensor to
+// vector d of the matching destination, as map(idx, so, d) sets them.  Each
+// thread issues the loads of U slots (U * NT vectors in flight) before its
+// first store, so a workgroup waits for one memory round trip per
+// U * NThreads slots instead of per NThreads.  The destinations must not
+// overlap the sources.
+//
+// The tensor count is a compile-time constant on purpose: behind a run-time
+// branch on the count (1, 2 or 3 tensors), the gfx950 code generator of ROCm
+// 7.2 structurized the three cases so that on the three-tensor path the
+// register holding the second destination's base address was never written,
+// and that store went to an unrelated address.
+template <int NT, int U, int NThreads, typename Map>
+__device__ __forceinline__ void copy_batched(const u32x4 *const (&src)[kMaxTensors],
+                                             u32x4 *const (&dst)[kMaxTensors], int total,
+                                             Map map) {
     static_assert(NT >= 1 && NT <= kMaxTensors, "1-3 tensors");
-    u32x4 x[NT];
+    for (int i0 = (int)threadIdx.x; i0 < total; i0 += NThreads * U) {
+        u32x4 x[U][NT];
+        int64_t dv[U];
+        bool ok[U];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) x[t] = src[t][so];
+        for (int u = 0; u < U; ++u) {
+            const int idx = i0 + u * NThreads;
+            ok[u] = idx < total;
+            int64_t sv = 0;
+            dv[u] = 0;
+            if (ok[u]) map(idx, sv, dv[u]);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) dst[t][d] = x[t];
+            for (int t = 0; t < NT; ++t) x[u][t] = ok[u] ? src[t][sv] : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (ok[u]) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t) dst[t][dv[u]] = x[u][t];
+            }
+        }
+    }
 }
 
 struct PackArgs {

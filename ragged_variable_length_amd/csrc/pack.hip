@@ -27,6 +27,7 @@ namespace rattn {
 namespace {
 
 constexpr int kPackThreads = 256;
+constexpr int kCopyBatch = 4;  // row-copy slots per thread with their loads in flight together
 constexpr int kScanThreads = 1024;
 constexpr int kScanWordsBig = 8;    // 16-byte mask words per thread and round, 1024-thread scan
 constexpr int kScanWordsSmall = 4;  // same, 256-thread scan inside the pack launch
@@ -222,13 +223,21 @@ __device__ __forceinline__ int rank_chunk(const uint8_t *keep_img, int cs, int c
     return __popcll(m);
 }
 
-// Kept tokens among positions [0, cs) of one image, counted by wave 0.
+// Kept tokens among positions [0, cs) of one image, counted by wave 0: eight
+// 64-position chunks per round, their mask loads issued together (one memory
+// round trip per 512 positions), then one ballot each.
 __device__ __forceinline__ int count_prefix_in_image(const uint8_t *keep_img, int cs) {
     const int lane = threadIdx.x & 63;
     int c = 0;
-    for (int n0 = 0; n0 < cs; n0 += 64) {
-        const int n = n0 + lane;
-        c += __popcll(__ballot(n < cs && keep_img[n] != 0));
+    for (int n0 = 0; n0 < cs; n0 += 64 * 8) {
+        uint8_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int n = n0 + 64 * u + lane;
+            v[u] = n < cs ? keep_img[n] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c += __popcll(__ballot(v[u] != 0));
     }
     return c;
 }
@@ -284,13 +293,13 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(PackArgs a) {
     const int rv = a.row_vec;
     const int total = kc * rv;
     const int64_t img_row0 = (int64_t)b * a.N;
-    for (int idx = tid; idx < total; idx += kPackThreads) {
-        const int j = idx / rv;
-        const int e = idx - j * rv;
-        const int64_t so = (img_row0 + list[j]) * rv + e;
-        const int64_t d = (base + j) * rv + e;
-        copy_vec<NT>(a.src, a.dst, so, d);
-    }
+    copy_batched<NT, kCopyBatch, kPackThreads>(
+        a.src, a.dst, total, [&](int idx, int64_t &so, int64_t &d) {
+            const int j = idx / rv;
+            const int e = idx - j * rv;
+            so = (img_row0 + list[j]) * rv + e;
+            d = (base + j) * rv + e;
+        });
 }
 
 // out[b, n] = kept ? src[rank] : 0 for the positions of one chunk; the chunk
@@ -315,13 +324,23 @@ __global__ __launch_bounds__(kPackThreads) void unpack_kernel(UnpackArgs a) {
     const int rv = a.row_vec;
     const u32x4 zero = {0u, 0u, 0u, 0u};
     if (a.dst) {
+        // kCopyBatch loads of a thread in flight before its first store
         const int total = (ce - cs) * rv;
         const int64_t out0 = ((int64_t)b * a.N + cs) * rv;
-        for (int idx = tid; idx < total; idx += kPackThreads) {
-            const int j = idx / rv;
-            const int e = idx - j * rv;
-            const int r = src_row[j];
-            a.dst[out0 + idx] = r >= 0 ? a.src[(int64_t)r * rv + e] : zero;
+        for (int i0 = tid; i0 < total; i0 += kPackThreads * kCopyBatch) {
+            u32x4 x[kCopyBatch];
+#pragma unroll
+            for (int u = 0; u < kCopyBatch; ++u) {
+                const int idx = i0 + u * kPackThreads;
+                const int j = idx / rv;
+                const int r = idx < total ? src_row[j] : -1;
+                x[u] = r >= 0 ? a.src[(int64_t)r * rv + (idx - j * rv)] : zero;
+            }
+#pragma unroll
+            for (int u = 0; u < kCopyBatch; ++u) {
+                const int idx = i0 + u * kPackThreads;
+                if (idx < total) a.dst[out0 + idx] = x[u];
+            }
         }
     }
     if (a.cls && cs == 0) {

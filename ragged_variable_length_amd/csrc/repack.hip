@@ -81,13 +81,13 @@ __global__ __launch_bounds__(kRepackThreads) void repack_kernel(RepackArgs a) {
         if (kept) list[off + before_in_wave] = r;
         __syncthreads();
         const int64_t dst_row0 = (int64_t)base + carry;
-        for (int idx = tid; idx < total * rv; idx += kRepackThreads) {
-            const int j = idx / rv;
-            const int p = idx - j * rv;
-            const int64_t so = (int64_t)list[j] * rv + p;
-            const int64_t d = (dst_row0 + j) * rv + p;
-            copy_vec<NT>(a.src, a.dst, so, d);
-        }
+        copy_batched<NT, 4, kRepackThreads>(
+            a.src, a.dst, total * rv, [&](int idx, int64_t &so, int64_t &d) {
+                const int j = idx / rv;
+                const int p = idx - j * rv;
+                so = (int64_t)list[j] * rv + p;
+                d = (dst_row0 + j) * rv + p;
+            });
         carry += total;
         __syncthreads();  // list and wave_cnt are rewritten by the next round
     }

@@ -8,7 +8,8 @@ address was left undefined (marked `implicit-def` in the assembly) and the
 store went to an unrelated address: an illegal memory access at run time.  The
 kernels now take the tensor count as a template parameter.  This test fails if
 any 16-byte store of a pack / re-pack kernel takes its base address from an
-SGPR pair that the compiler marks as undefined anywhere in that kernel.
+SGPR pair that, on some control-flow path to it, holds no value the program
+wrote (the compiler marks such a pair `implicit-def`).
 """
 import os
 import re
@@ -38,6 +39,99 @@ def _kernels(asm):
         yield m.group(1), [l.strip() for l in m.group(2).split("\n")]
 
 
+_LABEL = re.compile(r"^(\.LBB\d+_\d+|; %bb\.\d+):")
+_UNDEF = re.compile(r"implicit-def: ((?:\$sgpr\d+_?)+)")
+# VOP3b forms: the second operand is a scalar destination (carry / condition)
+_SDST2 = ("v_mad_u64_u32", "v_mad_i64_i32", "v_add_co_u32", "v_sub_co_u32", "v_subrev_co_u32",
+          "v_addc_co_u32", "v_subb_co_u32", "v_subbrev_co_u32", "v_div_scale")
+_NO_DST = ("s_cmp", "s_bitcmp", "s_cbranch", "s_branch", "s_waitcnt", "s_barrier", "s_nop",
+           "s_endpgm", "s_setprio", "s_sleep", "s_sendmsg", "s_trap", "s_dcache", "s_store",
+           "s_buffer_store", "s_set_gpr_idx", "s_setpc")
+
+
+def _sregs(op):
+    """Scalar registers named by one operand ('s7', 's[4:7]'), else empty."""
+    m = re.fullmatch(r"s(\d+)", op) or re.fullmatch(r"s\[(\d+):(\d+)\]", op)
+    if not m:
+        return set()
+    lo = int(m.group(1))
+    hi = int(m.group(2)) if m.lastindex == 2 else lo
+    return set(range(lo, hi + 1))
+
+
+def _defs(line):
+    """(registers written, written-as-undefined) by one assembly line."""
+    u = _UNDEF.search(line)
+    if u:
+        return {int(r) for r in re.findall(r"sgpr(\d+)", u.group(1))}, True
+    if not line or line.startswith((";", ".")):
+        return set(), False
+    parts = line.split(None, 1)
+    op = parts[0]
+    if op.startswith(_NO_DST) or len(parts) < 2:
+        return set(), False
+    ops = [o.strip() for o in parts[1].split(",")]
+    regs = _sregs(ops[0].split()[0])
+    if op.startswith(_SDST2) and len(ops) > 1:
+        regs |= _sregs(ops[1].split()[0])
+    return regs, False
+
+
+def _cfg(lines):
+    """Basic blocks (start, end) of a kernel and each block's predecessors."""
+    starts = [0] + [i for i, l in enumerate(lines) if _LABEL.match(l)]
+    starts = sorted(set(starts))
+    blocks = [(s_, e_) for s_, e_ in zip(starts, starts[1:] + [len(lines)])]
+    name_of = {}
+    for bi, (s_, _) in enumerate(blocks):
+        m = _LABEL.match(lines[s_])
+        if m:
+            name_of[m.group(1)] = bi
+    preds = {bi: set() for bi in range(len(blocks))}
+    for bi, (s_, e_) in enumerate(blocks):
+        body = [l for l in lines[s_:e_] if l and not l.startswith((";", "."))]
+        falls = True
+        for l in body:
+            op = l.split()[0]
+            if op.startswith(("s_cbranch", "s_branch")):
+                tgt = l.split()[1]
+                if tgt in name_of:
+                    preds[name_of[tgt]].add(bi)
+                if op == "s_branch":
+                    falls = False
+            if op in ("s_endpgm", "s_setpc_b64"):
+                falls = False
+        if falls and bi + 1 < len(blocks):
+            preds[bi + 1].add(bi)
+    return blocks, preds
+
+
+def _undefined_on_some_path(lines, blocks, preds, store_line, regs):
+    """True if, on some path into `store_line`, the nearest earlier write of
+    any register in `regs` is an implicit-def or there is none (kernel entry)."""
+    bi = next(b for b, (s_, e_) in enumerate(blocks) if s_ <= store_line < e_)
+    work, seen = [(bi, store_line)], set()
+    while work:
+        b, end = work.pop()
+        s_ = blocks[b][0]
+        hit = None
+        for i in range(end - 1, s_ - 1, -1):
+            w, undef = _defs(lines[i])
+            if w & regs:
+                hit = undef
+                break
+        if hit is None:
+            if b == 0 or not preds[b]:
+                return True
+            for pb in preds[b]:
+                if pb not in seen:
+                    seen.add(pb)
+                    work.append((pb, blocks[pb][1]))
+        elif hit:
+            return True
+    return False
+
+
 def _store_bases(lines):
     """(line index, 's[a:b]') for every 16-byte global store whose address is
     formed from an SGPR pair, directly or by the v_lshl_add_u64 that last wrote
@@ -54,23 +148,22 @@ def _store_bases(lines):
             if lines[j].startswith("v_") and lines[j].split(None, 1)[1].startswith(ops[0] + ","):
                 m = re.search(r"s\[\d+:\d+\]", lines[j])
                 if m:
-                    out.append((i, m.group(0)))
+                    out.append((j, m.group(0)))
                 break
     return out
 
 
 def _undefined_store_bases(asm, name_filter):
+    """Stores of the selected kernels whose SGPR base pair may hold no value
+    written by the program on some control-flow path to the address."""
     bad, checked = [], 0
     for name, lines in _kernels(asm):
         if not name_filter(name):
             continue
-        undefined = set()
-        for l in lines:
-            for a, b in re.findall(r"implicit-def: \$sgpr(\d+)_sgpr(\d+)", l):
-                undefined.add(f"s[{a}:{b}]")
+        blocks, preds = _cfg(lines)
         for i, base in _store_bases(lines):
             checked += 1
-            if base in undefined:
+            if _undefined_on_some_path(lines, blocks, preds, i, _sregs(base)):
                 bad.append((name, i, lines[i], base))
     return bad, checked
 
