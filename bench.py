@@ -441,7 +441,8 @@ def region_time_us(r: Resident, launches: int) -> float:
     return e0.elapsed_time(e1) * 1000.0 / launches
 
 
-def kernel_time_us(r: Resident, launches: int, cold: bool, flush_buf=None) -> float:
+def kernel_time_us(r: Resident, launches: int, cold: bool, flush_buf=None,
+                   cold_launches: int = 50) -> float:
     """Warm: region average of back-to-back launches.  Cold: median of single
     launches between HIP events, each after a 512 MB write that evicts the
     MALL (the events add about 2 us to each)."""
@@ -450,7 +451,7 @@ def kernel_time_us(r: Resident, launches: int, cold: bool, flush_buf=None) -> fl
     r.step()
     torch.cuda.synchronize()
     times = []
-    for _ in range(launches):
+    for _ in range(cold_launches):
         if cold:
             flush_buf.zero_()  # evict the 256 MB MALL between launches
         e0 = torch.cuda.Event(enable_timing=True)
@@ -464,7 +465,7 @@ def kernel_time_us(r: Resident, launches: int, cold: bool, flush_buf=None) -> fl
     return times[len(times) // 2]
 
 
-def forward_alone(w, stream, launches: int, flush_buf) -> dict:
+def forward_alone(w, stream, launches: int, flush_buf, cold_launches: int) -> dict:
     """rattn_forward alone on the flat buffers of a workload (prepared on the
     host, resident in HBM), against its own algorithmic bytes (q, k, v read and
     o written once): warm, back-to-back region average from C++; cold, median
@@ -475,7 +476,7 @@ def forward_alone(w, stream, launches: int, flush_buf) -> dict:
     lib = timing_lib()
     warm = c_region_us(step, WHAT_FORWARD, launches, stream)
     times = []
-    for _ in range(launches):
+    for _ in range(cold_launches):
         flush_buf.zero_()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -513,7 +514,7 @@ def padded_comparison(r: Resident, launches: int) -> dict:
     return out
 
 
-def large_configs(stream, launches: int) -> dict:
+def large_configs(stream, launches: int, cold_launches: int) -> dict:
     out = {}
     flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device="cuda")
     for name, maker in (("deit_b_384_50pct", workloads.deit_b_384),
@@ -527,9 +528,9 @@ def large_configs(stream, launches: int) -> dict:
                "traffic_bytes": measured_traffic(w.name)}
         row["padded_comparator"] = padded_comparison(r, launches)
         row["three_call_and_stacks"] = three_call_and_stacks(r, launches)
-        row["forward_alone"] = forward_alone(w, stream, launches, flush)
+        row["forward_alone"] = forward_alone(w, stream, launches, flush, cold_launches)
         for cold in (False, True):
-            us = kernel_time_us(r, launches, cold, flush)
+            us = kernel_time_us(r, launches, cold, flush, cold_launches)
             gbs = nbytes / (us * 1e-6) / 1e9
             tfl = flops / (us * 1e-6) / 1e12
             row["cold" if cold else "warm"] = {
@@ -678,7 +679,7 @@ def main():
         _print_stacks(w.name, line["three_call_and_stacks"])
         side = torch.cuda.Stream()  # graph capture needs a non-default stream
         line["dispatch_floor"] = dispatch_floors(side, iters=1000, warmup=100)
-        line["large_configs"] = large_configs(stream, launches=50)
+        line["large_configs"] = large_configs(stream, launches=300, cold_launches=50)
     if not args.quick and not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(line), flush=True)
