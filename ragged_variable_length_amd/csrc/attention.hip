@@ -14,33 +14,42 @@
 // kept rows j of the same image.
 //
 // CDNA4 mapping (16-bit inputs):
-//  * One workgroup = 4 wavefronts = one (image, head, 64-query tile); each
-//    wavefront owns 16 query rows.  Workgroup ids are laid out so all query
-//    tiles of one (image, head) land on the same XCD (ids are dealt to the 8
-//    XCDs round-robin), keeping that head's K/V rows in one L2.
-//  * Keys stream through LDS in chunks of 64, double-buffered: the global
-//    loads of chunk c+1 are in flight while chunk c is computed, one barrier
-//    per chunk.  K is stored row-major, V transposed (dims x keys) so each
-//    MFMA operand is one 16-byte LDS read per lane; 16-byte pieces of a row
-//    are XOR-swizzled by (row & 7) so the 16 rows one operand read touches hit
-//    distinct banks without padding.
+//  * A workgroup is W wavefronts, each owning QB blocks of 16 query rows, so
+//    a query tile is 16*W*QB rows (4x1: 64 rows up to 256 positions, 4x2:
+//    128 rows beyond).  The query tiles of one (image, head) go to G
+//    workgroups (tiles g, g+G, ...); G > 1 only when the batch has fewer
+//    heads than the chip has CUs.  Workgroup ids are laid out so that the G
+//    workgroups of one (image, head) land on the same XCD (ids are dealt to
+//    the 8 XCDs round-robin), keeping that head's K/V rows in one L2.
+//  * Keys stream through LDS in chunks of 64, double-buffered, copied by
+//    global->LDS DMA (global_load_lds_dwordx4, 16 bytes per lane straight
+//    into the lane's LDS slot).  The copy of the next step's chunk is in
+//    flight while the current one is computed, one barrier per step; a
+//    sequence of at most two chunks stays resident.  16-byte pieces of each
+//    K and V row are XOR-permuted so that the operand reads hit distinct
+//    banks without padding.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_16x16x32_{bf16,f16}: in the accumulator layout each lane holds
-//    4 keys of ONE query, so the running max / sum are per-lane scalars (the
-//    max needs two cross-lane steps per chunk, the sum none until the end).
-//  * The probabilities feed O^T = V^T P^T directly as the MFMA B operand: the
-//    V^T column order is permuted so operand slot (lane group g, slot s) of a
-//    32-key step carries the same key in V^T and in the score accumulators.
-//  * Online softmax in base 2: scores times scale*log2(e), v_exp_f32, running
-//    output rescaled by exp2(m_old - m_new) per chunk, one division at the end.
-//  * Keys past the sequence end inside the last chunk are zero-filled in LDS
-//    and get score -inf; query rows past the end are computed on zeros and
-//    never stored.
+//    4 keys of ONE query, so the running max and sum are per-lane scalars (the
+//    max needs two cross-lane steps per chunk, the sum none: it comes from one
+//    more MFMA against an all-ones operand).
+//  * The probabilities feed O^T = V^T P^T directly as the MFMA B operand;
+//    V^T is read with the transposing LDS read ds_read_b64_tr_b16, its key
+//    order matching the score accumulators slot for slot.
+//  * Online softmax in base 2 (scores times scale*log2(e), v_exp_f32).  For
+//    scale > 0 the reference max may lag the running max by 8 in log2 units:
+//    the output and row sum are rescaled only when some row's max grows past
+//    that, and the final division cancels whichever reference was used.
+//  * Copies of keys past the sequence end read the last key's row (finite
+//    values) and their scores are set to -inf, so every copy runs with all
+//    lanes active; query rows past the end are computed on zeros and never
+//    stored.
 //  * Fused path: the workgroup first ranks its image's kept tokens with one
 //    wavefront ballot per 64 positions into an LDS list of positions; Q/K/V
-//    rows are then read from those positions of the padded tensors and the
-//    outputs written to the same positions of the padded output.  Tile 0 of
-//    each (image, head) also writes zeros to the pruned rows and the CLS row.
+//    rows are then copied from those positions of the padded tensors and the
+//    outputs written to the same positions of the padded output.  After its
+//    attention, the last workgroup of each (image, head) writes zeros to the
+//    pruned rows and, when position 0 was pruned, the CLS row.
 // The float32 path has the same structure on v_mfma_f32_16x16x4_f32 with
 // 32-key chunks, row-padded LDS and probabilities kept in float32.
 #include <algorithm>
@@ -669,10 +678,6 @@ struct Shape {
 };
 
 Shape shape_for(int max_seqlen) {
-#if defined(RATTN_FORCE_W) && defined(RATTN_FORCE_QB)
-    (void)max_seqlen;
-    return Shape{RATTN_FORCE_W, RATTN_FORCE_QB};
-#else
     // measured on MI355X (rattn_fused, back to back): up to 256 positions
     // 4x1 is best (batch 512: 52 us; 4x2 56, 8x1 61); at 577 positions 4x2
     // (56 us) beats 8x1 (60) and 4x1 (69): its 128-row tiles stream K/V three
@@ -680,7 +685,6 @@ Shape shape_for(int max_seqlen) {
     // a 64-image batch run in one round
     if (max_seqlen <= 256) return Shape{4, 1};
     return Shape{4, 2};
-#endif
 }
 
 int64_t grid_for(int B, int H, int G) { return 8 * (((int64_t)B * H + 7) / 8) * G; }
