@@ -421,6 +421,21 @@ def dispatch_floors(stream, iters: int, warmup: int) -> dict:
               f" enqueue {row['fused_enqueue_us']['median_us']} us, rattn_forward alone call+sync "
               f"{row['forward_call_sync_us']['median_us']} us, three calls + sync "
               f"{row['three_call_call_sync_us']['median_us']} us", flush=True)
+    # every point of the serving sweep: the one launch, host call + sync and
+    # device time back to back
+    sweep = {}
+    for B, p, exact in workloads.sweep_points():
+        r = Resident(workloads.deit_b_sweep(B, p, exact_unpruned=exact), stream)
+        cs = r.c_step()
+        if lib.bench_call_floor(ctypes.byref(cs), WHAT_FUSED, iters, warmup, ctypes.byref(st)):
+            raise RuntimeError("bench_call_floor failed")
+        sweep[r.w.name] = {"B": B, "prune": p, "T": r.T, "fused_call_sync_us": st.median_us,
+                           "fused_device_us": round(c_region_us(cs, WHAT_FUSED, iters, stream), 2)}
+    res["sweep"] = sweep
+    print("[bench] serving sweep, rattn_fused call+sync (device) us: " + ", ".join(
+        f"B{v['B']} p{int(round(v['prune'] * 100))}{'x' if 'exact' in k else ''} "
+        f"{v['fused_call_sync_us']:.1f} ({v['fused_device_us']:.1f})" for k, v in sweep.items()),
+        flush=True)
     return res
 
 
@@ -497,20 +512,28 @@ def forward_alone(w, stream, launches: int, flush_buf, cold_launches: int) -> di
     return out
 
 
-def padded_comparison(r: Resident, launches: int) -> dict:
+def padded_comparison(r: Resident, launches: int, rounds: int = 3) -> dict:
     """The ragged kernel against its dense comparator (rattn_fused_padded,
     same outputs): every image padded to the longest survivor, and to N (no
-    pruning gain at all), warm back-to-back averages."""
-    out = {"ragged_us": round(region_time_us(r, launches), 2)}
-    saved = r.step
+    pruning gain at all).  Warm back-to-back averages; the three are measured
+    in turn, `rounds` times, and each reports its median, so that the first
+    one measured does not absorb the GPU's ramp-up."""
+    plans = {"ragged": r.plan.run}
     for name, pad in (("padded_longest", max(r.lengths)), ("padded_n", r.w.N)):
-        plan = FusedPlan(r.q, r.k, r.v, r.keep, r.w.scale, out_padded=r.out, cls=r.cls,
-                         stream=r.stream, pad_len=max(pad, 1))
-        r.step = plan.run
-        us = region_time_us(r, launches)
-        out[f"{name}_us"] = round(us, 2)
-        out[f"ragged_speedup_vs_{name}"] = round(us / out["ragged_us"], 3)
+        plans[name] = FusedPlan(r.q, r.k, r.v, r.keep, r.w.scale, out_padded=r.out, cls=r.cls,
+                                stream=r.stream, pad_len=max(pad, 1)).run
+    times = {name: [] for name in plans}
+    saved = r.step
+    for _ in range(rounds):
+        for name, run in plans.items():
+            r.step = run
+            times[name].append(region_time_us(r, launches))
     r.step = saved
+    med = {name: sorted(t)[len(t) // 2] for name, t in times.items()}
+    out = {"ragged_us": round(med["ragged"], 2)}
+    for name in ("padded_longest", "padded_n"):
+        out[f"{name}_us"] = round(med[name], 2)
+        out[f"ragged_speedup_vs_{name}"] = round(med[name] / med["ragged"], 3)
     return out
 
 
@@ -563,6 +586,26 @@ def _print_stacks(name: str, t: dict) -> None:
           f" {st['layers']} layers packed once {st['packed_once_us']} us vs rattn_fused per layer "
           f"{st['fused_per_layer_us']} us ({st['packed_speedup_vs_fused_per_layer']}x); re-pack "
           f"{t['repack']['us']} us ({t['repack']['hbm_frac']:.3f} of HBM)", flush=True)
+
+
+def box_copy_bandwidth(stream, nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """Device-to-device copy of a 1 GiB buffer (the runtime's copy kernel):
+    bytes read plus bytes written per second, GB/s -- the box's own measure
+    of the HBM roof, next to the 8 TB/s datasheet figure."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record(stream)
+    e1.synchronize()
+    sec = e0.elapsed_time(e1) / 1000.0 / reps
+    del a, b
+    return round(2 * nbytes / sec / 1e9, 1)
 
 
 def cpu_baseline(w, budget_s: float) -> dict:
@@ -671,6 +714,18 @@ def main():
         "roofline": roofline,
     }
     if not args.quick:
+        box = box_copy_bandwidth(stream)
+        roofline["box_peak_GBps"] = box
+        roofline["box_peak_from"] = "1 GiB device-to-device copy, read + written bytes / time"
+        roofline["box_frac"] = round(achieved / box, 5)
+        print(f"[bench] box-measured copy bandwidth {box} GB/s", flush=True)
+        flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device="cuda")
+        cold = kernel_time_us(r, K, True, flush, cold_launches=200)
+        del flush
+        line["cold"] = {"us": round(cold, 2), "hbm_frac": round(nbytes / (cold * 1e-6) / 1e9 / HBM_PEAK_GBS, 5),
+                        "from": "median of single launches between HIP events, each after a 512 MB write "
+                                "that evicts the 256 MB MALL"}
+        print(f"[bench] {w.name}: cold {cold:.2f} us per launch", flush=True)
         line["padded_comparator"] = padded_comparison(r, K)
         pc = line["padded_comparator"]
         print(f"[bench] {w.name}: ragged {pc['ragged_us']} us, padded to longest survivor "
