@@ -608,6 +608,24 @@ def box_copy_bandwidth(stream, nbytes: int = 1 << 30, reps: int = 10) -> float:
     return round(2 * nbytes / sec / 1e9, 1)
 
 
+def tiny_fp32(stream, launches: int) -> dict:
+    """The tiny float32 workload (B=4, N=197, H=3): rattn_fused warm, back to
+    back, against both roofs -- float32 matrix/vector arithmetic binds here,
+    not HBM, and at this size the launch itself is most of the time."""
+    w = workloads.tiny()
+    r = Resident(w, stream)
+    us = region_time_us(r, launches)
+    flops = attention_flops(r.lengths, w.H)
+    nbytes = fused_bytes(r.T, w.B, w.N, w.H, w.dtype)
+    out = {"B": w.B, "N": w.N, "H": w.H, "dtype": w.dtype, "T": r.T, "us": round(us, 2),
+           "attn_flops": flops, "fused_bytes": nbytes,
+           "fp32_frac": round(flops / (us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS["f32"], 5),
+           "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 5)}
+    print(f"[bench] {w.name}: rattn_fused {us:.2f} us (fp32 {out['fp32_frac']:.4f} of the "
+          f"157.3 TFLOP/s roof, HBM {out['hbm_frac']:.4f})", flush=True)
+    return out
+
+
 def cpu_baseline(w, budget_s: float) -> dict:
     """The CPU oracle (plain C, fp64, one thread) on the same workload: whole
     batches of scan, pack, attention and unpack until the budget is used."""
@@ -735,6 +753,7 @@ def main():
         side = torch.cuda.Stream()  # graph capture needs a non-default stream
         line["dispatch_floor"] = dispatch_floors(side, iters=1000, warmup=100)
         line["large_configs"] = large_configs(stream, launches=300, cold_launches=50)
+        line["tiny_fp32"] = tiny_fp32(stream, launches=2000)
     if not args.quick and not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(line), flush=True)

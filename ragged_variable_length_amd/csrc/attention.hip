@@ -490,13 +490,14 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
 }
 
 // ---------------------------------------------------------------------------
-// float32 core: all 64-query tiles of one (image, head), 32-key chunks
+// float32 core: the 64-query tiles g, g+G, ... of one (image, head), 32-key
+// chunks
 // ---------------------------------------------------------------------------
 template <typename Rows>
 __device__ __forceinline__ void attend32(const float *__restrict__ q, const float *__restrict__ k,
                                          const float *__restrict__ v, float *__restrict__ o,
-                                         const Rows &R, int L, int Lp, float c, float *sK,
-                                         float *sV, float *__restrict__ cls_dst) {
+                                         const Rows &R, int L, int Lp, float c, int g, int G,
+                                         float *sK, float *sV, float *__restrict__ cls_dst) {
     // Lp >= L: length processed (padded comparator), as in the 16-bit core
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
@@ -532,7 +533,7 @@ __device__ __forceinline__ void attend32(const float *__restrict__ q, const floa
     const int nch = (Lp + kKC32 - 1) / kKC32;
     const int ntile = (Lp + kQT - 1) / kQT;
     const bool resident = nch <= 2;
-    for (int t = 0; t < ntile; ++t) {
+    for (int t = g; t < ntile; t += G) {
         // B operand of score step kk: Q[query col][4*kk + grp]
         const int qrow = t * kQT + wid * kQW + col;
         float qf[16];
@@ -541,7 +542,7 @@ __device__ __forceinline__ void attend32(const float *__restrict__ q, const floa
 #pragma unroll
             for (int kk = 0; kk < 16; ++kk) qf[kk] = qrow < L ? src[4 * kk + grp] : 0.f;
         }
-        const bool stage = !resident || t == 0;
+        const bool stage = !resident || t == g;
         if (stage) {
             RATTN_LOAD32(0)
             RATTN_STORE32(0)
@@ -627,12 +628,6 @@ __device__ __forceinline__ void attend32(const float *__restrict__ q, const floa
     }
 #undef RATTN_LOAD32
 #undef RATTN_STORE32
-}
-
-// (image, head) of a one-workgroup-per-head launch.
-__device__ __forceinline__ void decode_pair(int H, int *b, int *h) {
-    *b = blockIdx.x / H;
-    *h = blockIdx.x - *b * H;
 }
 
 // (image, head, tile group) of this workgroup; false if the id is padding.
@@ -723,19 +718,19 @@ __global__ __launch_bounds__(kThreads) void attn_fwd32(const float *__restrict__
                                                        const float *__restrict__ k,
                                                        const float *__restrict__ v,
                                                        float *__restrict__ o,
-                                                       const int32_t *__restrict__ cu, int H,
-                                                       int max_seqlen, float c) {
+                                                       const int32_t *__restrict__ cu, int B,
+                                                       int H, int G, int max_seqlen, float c) {
     __shared__ __attribute__((aligned(16))) float sK[2 * kKC32 * kLd32];
     __shared__ __attribute__((aligned(16))) float sV[2 * kKC32 * kLd32];
-    int b, h;
-    decode_pair(H, &b, &h);
+    int b, h, g;
+    if (!decode_group(B * H, H, G, &b, &h, &g)) return;
     const int seq0 = cu[b];
     const int L = cu[b + 1] - seq0;
     if (L <= 0 || L > max_seqlen) return;
     const int64_t rs = (int64_t)H * kD;
     const int64_t base = (int64_t)seq0 * rs + (int64_t)h * kD;
     const FlatRows R = {(uint32_t)rs};
-    attend32(q + base, k + base, v + base, o + base, R, L, L, c, sK, sV, nullptr);
+    attend32(q + base, k + base, v + base, o + base, R, L, L, c, g, G, sK, sV, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -858,14 +853,14 @@ __global__ __launch_bounds__(kThreads) void fused32(const float *__restrict__ q,
                                                     const float *__restrict__ v,
                                                     const uint8_t *__restrict__ keep,
                                                     float *__restrict__ out,
-                                                    float *__restrict__ cls, int N, int H,
-                                                    int pad, float c) {
+                                                    float *__restrict__ cls, int B, int N,
+                                                    int H, int G, int pad, float c) {
     __shared__ __attribute__((aligned(16))) float sK[2 * kKC32 * kLd32];
     __shared__ __attribute__((aligned(16))) float sV[2 * kKC32 * kLd32];
     __shared__ int16_t pos[kMaxFusedN];
     __shared__ uint64_t keep_bits[kMaxFusedN / 64];
-    int b, h;
-    decode_pair(H, &b, &h);
+    int b, h, g;
+    if (!decode_group(B * H, H, G, &b, &h, &g)) return;
     const uint8_t *keep_img = keep + (int64_t)b * N;
     const int L = rank_image<kWaves>(keep_img, N, pos, keep_bits);
     const int64_t rs = (int64_t)H * kD;
@@ -875,12 +870,25 @@ __global__ __launch_bounds__(kThreads) void fused32(const float *__restrict__ q,
     if (L > 0) {
         const PaddedRows R = {(uint32_t)rs, pos};
         float *cls_dst = (cls_head && pos[0] == 0) ? cls_head : nullptr;
-        if (out || cls_dst)
-            attend32(q + head0, k + head0, v + head0, out_head, R, L, max(L, pad), c, sK, sV,
+        const int Lp = max(L, pad);
+        int gg = g, GG = G;
+        bool run = true;
+        if (!out) {
+            // CLS rows only: the workgroup holding query tile 0 computes that
+            // tile alone
+            run = cls_dst && g == 0;
+            GG = (Lp + kQT - 1) / kQT;
+            gg = 0;
+        }
+        if (run)
+            attend32(q + head0, k + head0, v + head0, out_head, R, L, Lp, c, gg, GG, sK, sV,
                      cls_dst);
     }
-    zero_pruned<kD * 4 / 16, kThreads>(keep_bits, N, out_head ? (u32x4 *)out_head : nullptr,
-                                       rs * 4 / 16, (u32x4 *)cls_head);
+    // zeros for the pruned rows: by the last workgroup of the head, after its
+    // attention
+    if (g == G - 1)
+        zero_pruned<kD * 4 / 16, kThreads>(keep_bits, N, out_head ? (u32x4 *)out_head : nullptr,
+                                           rs * 4 / 16, (u32x4 *)cls_head);
 }
 
 template <typename T, int W, int QB>
@@ -928,11 +936,13 @@ hipError_t launch_attention(const AttnArgs &a, hipStream_t s) {
     switch (a.dt) {
     case Elem::BF16: launch_fwd16_shape<__bf16>(a, c, s); break;
     case Elem::F16: launch_fwd16_shape<_Float16>(a, c, s); break;
-    case Elem::F32:
-        hipLaunchKernelGGL(attn_fwd32, dim3((unsigned)((int64_t)a.B * a.H)), dim3(kThreads), 0, s,
+    case Elem::F32: {
+        const int G = tile_groups(a.B, a.H, a.max_seqlen, kQT, false);
+        hipLaunchKernelGGL(attn_fwd32, dim3((unsigned)grid_for(a.B, a.H, G)), dim3(kThreads), 0, s,
                            (const float *)a.q, (const float *)a.k, (const float *)a.v,
-                           (float *)a.o, a.cu, a.H, a.max_seqlen, c);
+                           (float *)a.o, a.cu, a.B, a.H, G, a.max_seqlen, c);
         break;
+    }
     }
     return hipGetLastError();
 }
@@ -942,11 +952,14 @@ hipError_t launch_fused(const FusedArgs &a, hipStream_t s) {
     switch (a.dt) {
     case Elem::BF16: launch_fused16_shape<__bf16>(a, c, s); break;
     case Elem::F16: launch_fused16_shape<_Float16>(a, c, s); break;
-    case Elem::F32:
-        hipLaunchKernelGGL(fused32, dim3((unsigned)((int64_t)a.B * a.H)), dim3(kThreads), 0, s,
+    case Elem::F32: {
+        // without the padded output only tile 0 (the CLS row) is computed
+        const int G = a.out ? tile_groups(a.B, a.H, std::min(a.max_seqlen, a.N), kQT, true) : 1;
+        hipLaunchKernelGGL(fused32, dim3((unsigned)grid_for(a.B, a.H, G)), dim3(kThreads), 0, s,
                            (const float *)a.q, (const float *)a.k, (const float *)a.v, a.keep,
-                           (float *)a.out, (float *)a.cls, a.N, a.H, a.pad, c);
+                           (float *)a.out, (float *)a.cls, a.B, a.N, a.H, G, a.pad, c);
         break;
+    }
     }
     return hipGetLastError();
 }
