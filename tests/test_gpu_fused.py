@@ -234,6 +234,22 @@ def test_fused_cls_only_matches_full():
     assert np.array_equal(bits(cls_only), bits(cls_full))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_fused_cls_only_several_tiles(dtype):
+    """CLS rows only, with two to three 64-row query tiles per head: only the
+    tile holding row 0 is computed, and it gives the full run's bits."""
+    keep = torch.zeros((4, 197), dtype=torch.uint8)
+    g = torch.Generator().manual_seed(31)
+    for b, L in enumerate((150, 197, 65, 129)):
+        keep[b, torch.randperm(197, generator=g)[:L]] = 1
+    keep[1:, 0] = 1  # image 0 may have lost its CLS row; the others keep it
+    w = workloads.custom(4, 197, 3, dtype, keep=keep, seed=32, name=f"cls_only_{dtype}")
+    say(f"CLS rows only, several tiles, {dtype}")
+    _, cls_full = run_fused(w)
+    _, cls_only = run_fused(w, want_out=False)
+    assert np.array_equal(bits(cls_only), bits(cls_full))
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.125, 0.5])
 def test_fused_unusual_scales(scale):
     full(workloads.custom(4, 90, 2, "bf16", p_keep=0.7, seed=17, scale=scale,
