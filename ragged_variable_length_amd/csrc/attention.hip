@@ -40,10 +40,14 @@
 //    scale > 0 the reference max may lag the running max by 8 in log2 units:
 //    the output and row sum are rescaled only when some row's max grows past
 //    that, and the final division cancels whichever reference was used.
+//  * With two blocks per wavefront (4x2) each wavefront copies its own Q rows
+//    into LDS by the same DMA and reads its operands from there every step,
+//    which keeps 32 VGPRs of current and prefetched Q rows out of the loop.
 //  * Copies of keys past the sequence end read the last key's row (finite
-//    values) and their scores are set to -inf, so every copy runs with all
-//    lanes active; query rows past the end are computed on zeros and never
-//    stored.
+//    values): their scores repeat a valid score, so the row max needs no
+//    mask, and they are set to -inf before the exponentials, so every copy
+//    runs with all lanes active.  Query rows past the end are computed on
+//    zeros (4x1) or copies of the last row (4x2) and never stored.
 //  * Fused path: the workgroup first ranks its image's kept tokens with one
 //    wavefront ballot per 64 positions into an LDS list of positions; Q/K/V
 //    rows are then copied from those positions of the padded tensors and the
@@ -190,7 +194,7 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
                                          const uint16_t *__restrict__ vh,
                                          uint16_t *__restrict__ oh, const Rows &R, int L, int Lp,
                                          float c, int g, int G, uint16_t *sK, uint16_t *sV,
-                                         uint16_t *__restrict__ cls_dst) {
+                                         uint16_t *sQ, uint16_t *__restrict__ cls_dst) {
     // Lp >= L is the length processed: L for ragged attention; for the padded
     // comparator, the padded length, whose extra keys are masked and whose
     // extra query rows are computed on zeros and discarded
@@ -249,6 +253,28 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
             }
         }
     };
+    // With two blocks per wavefront the Q rows live in LDS instead of
+    // registers (32 VGPRs for the current and the prefetched tile would
+    // otherwise be live across the loop): each wavefront copies its own rows
+    // of a query tile by global->LDS DMA, in K's swizzled layout, and reads
+    // its B operands from there every step.  No other wavefront touches
+    // them, so no barrier guards them; the next tile's rows are copied as
+    // soon as the last chunk's S^T has read the current ones.  Rows past the
+    // sequence end copy the last row (finite values, never stored).
+    constexpr bool kQL = QB == 2;
+    auto stage_q = [&](int tile) {
+        constexpr int kQDma = kRowsPerWave / 8;
+        uint32_t ro[kQDma];
+#pragma unroll
+        for (int i = 0; i < kQDma; ++i)
+            ro[i] = R.off(min(tile * kQT16 + wid * kRowsPerWave + 8 * i + srow, L - 1));
+#pragma unroll
+        for (int i = 0; i < kQDma; ++i) {
+            const int row0 = wid * kRowsPerWave + 8 * i;
+            __builtin_amdgcn_global_load_lds(qh + ro[i] + 8 * kpiece(row0 + srow, sslot),
+                                             RATTN_LDS(sQ + row0 * 64), 16, 0, 0);
+        }
+    };
 
     // This workgroup owns query tiles g, g+G, g+2G, ... of the sequence; G
     // workgroups share one (image, head).  Keys come in nch chunks of 64.
@@ -264,8 +290,9 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
     int t = g, ch = 0, step = 0;
     u32x4 qf0[QB], qf1[QB], qn0[QB], qn1[QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) qn0[qb] = qn1[qb] = zero4;
-    load_q(t, qf0, qf1);
+    for (int qb = 0; qb < QB; ++qb) qf0[qb] = qf1[qb] = qn0[qb] = qn1[qb] = zero4;
+    if constexpr (kQL) stage_q(t);
+    else load_q(t, qf0, qf1);
     stage(0, 0);
     if (resident && nch == 2) {
         // both chunks in flight at once; wait for the Q rows and chunk 0
@@ -306,7 +333,7 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
         const bool next_tile = has_next && nc == 0;
         const bool load_next = !resident && has_next;
         if (load_next) stage(nc, (step + 1) & 1);
-        if (next_tile) load_q(nt, qn0, qn1);
+        if (!kQL && next_tile) load_q(nt, qn0, qn1);
 
         const int buf = resident ? ch : (step & 1);
         const uint16_t *Ks = sK + buf * (kKC * 64);
@@ -316,12 +343,27 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
 
         // A wavefront whose query rows all lie past the sequence end has
         // nothing to compute (it still stages and meets every barrier).
-        if (t * kQT16 + wid * kRowsPerWave < Lp) {
-            // S^T for the 64 keys of the chunk.  Every block is computed:
-            // rows of keys past the end hold copies of the last key, whose
-            // scores are replaced by -inf below, so no branch sits between
-            // the reads.  Each K operand serves all QB query blocks.
-            f32x4 s[QB][4];
+        const bool active = t * kQT16 + wid * kRowsPerWave < Lp;
+        f32x4 s[QB][4];
+        float mx[QB];
+        if (active) {
+            if constexpr (kQL) {
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) {
+                    const int r = wid * kRowsPerWave + qb * kQW + col;
+                    qf0[qb] = *(const u32x4 *)(sQ + r * 64 + 8 * kpiece(r, grp));
+                    qf1[qb] = *(const u32x4 *)(sQ + r * 64 + 8 * kpiece(r, 4 + grp));
+                }
+            }
+            // S^T for the 64 keys of the chunk, with each block's row maximum
+            // taken as soon as its scores are done.  Every block is computed:
+            // rows of keys past the end hold copies of the last key, so no
+            // branch sits between the reads, their scores repeat a valid one
+            // (the maximum over all 64 is the maximum over the valid keys),
+            // and they are masked to -inf only before the exponentials.  Each
+            // K operand serves all QB query blocks.
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) mx[qb] = -INFINITY;
 #pragma unroll
             for (int blk = 0; blk < 4; ++blk) {
                 const int row = 16 * blk + col;
@@ -333,6 +375,42 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
                     z = Mma<T>::run(__builtin_bit_cast(V8, a0), __builtin_bit_cast(V8, qf0[qb]), z);
                     s[qb][blk] = Mma<T>::run(__builtin_bit_cast(V8, a1),
                                              __builtin_bit_cast(V8, qf1[qb]), z);
+                    if constexpr (kPos) {
+                        const float t3 = vmax(vmax(s[qb][blk][0], s[qb][blk][1]), s[qb][blk][2]);
+                        mx[qb] = vmax(vmax(mx[qb], t3), s[qb][blk][3]);
+                    }
+                }
+            }
+        }
+        // the Q operands of this tile have been read: copy the next tile's
+        if (kQL && next_tile) stage_q(nt);
+        if (active) {
+            if constexpr (kPos) {
+                // scale > 0: the largest score is the largest raw dot
+                // product, so the reference max m is kept in raw units and
+                // each probability is one fma and one exp2.  m may lag the
+                // running max by up to kLag / c (probabilities up to 2^kLag):
+                // the output and the row sum are rescaled only when some
+                // row's max grows past that, which after the first chunk is
+                // rare, and the final division cancels whichever reference
+                // was used.  One test covers all blocks, on each lane's own
+                // maximum: some lane's exceeds m + lag exactly when the
+                // maximum over the four lanes of that query does, so the
+                // cross-lane reduction runs only when rescaling.
+                bool grow = false;
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) grow = grow || mx[qb] > m[qb] + lag;
+                if (__ballot(grow)) {
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb) {
+                        const float mn = vmax(m[qb], max_across_groups(mx[qb]));
+                        const float alpha = fast_exp2((m[qb] - mn) * c);
+                        m[qb] = mn;
+                        mc[qb] = mn * c;
+#pragma unroll
+                        for (int dt = 0; dt < 4; ++dt) acc[qb][dt] *= alpha;
+                        accl[qb][0] *= alpha;
+                    }
                 }
             }
             if (valid < kKC) {
@@ -347,29 +425,6 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 if constexpr (kPos) {
-                    // scale > 0: the largest score is the largest raw dot
-                    // product, so the reference max m is kept in raw units
-                    // and each probability is one fma and one exp2.  m may
-                    // lag the running max by up to kLag / c (probabilities up
-                    // to 2^kLag): the output and the row sum are rescaled only
-                    // when some row's max grows past that, which after the
-                    // first chunk is rare, and the final division cancels
-                    // whichever reference was used.
-                    float mx = vmax(vmax(s[qb][0][0], s[qb][0][1]), vmax(s[qb][0][2], s[qb][0][3]));
-#pragma unroll
-                    for (int blk = 1; blk < 4; ++blk)
-                        mx = vmax(vmax(mx, vmax(s[qb][blk][0], s[qb][blk][1])),
-                                  vmax(s[qb][blk][2], s[qb][blk][3]));
-                    mx = max_across_groups(mx);
-                    if (__ballot(mx > m[qb] + lag)) {
-                        const float mn = vmax(m[qb], mx);
-                        const float alpha = fast_exp2((m[qb] - mn) * c);
-                        m[qb] = mn;
-                        mc[qb] = mn * c;
-#pragma unroll
-                        for (int dt = 0; dt < 4; ++dt) acc[qb][dt] *= alpha;
-                        accl[qb][0] *= alpha;
-                    }
 #pragma unroll
                     for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
@@ -378,17 +433,17 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
                 } else {
                     // scale <= 0 (degenerate but valid): scale, then the
                     // exact running max (masked scores stay -inf)
-                    float mx = -INFINITY;
+                    float mxn = -INFINITY;
 #pragma unroll
                     for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const float x = s[qb][blk][i] == -INFINITY ? -INFINITY : s[qb][blk][i] * c;
                             s[qb][blk][i] = x;
-                            mx = fmaxf(mx, x);
+                            mxn = fmaxf(mxn, x);
                         }
-                    mx = max_across_groups(mx);
-                    const float mn = fmaxf(m[qb], mx);
+                    mxn = max_across_groups(mxn);
+                    const float mn = fmaxf(m[qb], mxn);
                     const float alpha = fast_exp2(m[qb] - mn);
                     m[qb] = mn;
 #pragma unroll
@@ -473,10 +528,10 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
         }
         // the next step's chunk has landed: the one staged in this step, or,
         // resident, chunk 1 staged up front
-        if (load_next || (resident && step == 0 && nch == 2)) wait_vmem();
+        if (load_next || (kQL && next_tile) || (resident && step == 0 && nch == 2)) wait_vmem();
         __syncthreads();
         if (!has_next) break;
-        if (next_tile) {
+        if (!kQL && next_tile) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 qf0[qb] = qn0[qb];
@@ -696,6 +751,7 @@ __global__ __launch_bounds__(64 * W, QB == 1 ? 4 : 3) void attn_fwd16(const uint
                                                         int H, int G, int max_seqlen, float c) {
     __shared__ __attribute__((aligned(16))) uint16_t sK[2 * kKC * 64];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2 * kD * 64];
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[QB == 2 ? 16 * W * QB * kD : 8];
     int b, h, g;
     if (!decode_group(B * H, H, G, &b, &h, &g)) return;
     const int seq0 = cu[b];
@@ -708,10 +764,10 @@ __global__ __launch_bounds__(64 * W, QB == 1 ? 4 : 3) void attn_fwd16(const uint
     const FlatRows R = {(uint32_t)rs};
     if (c > 0.f)
         attend16<T, true, W, QB>(q + base, k + base, v + base, o + base, R, L, L, c, g, G, sK, sV,
-                                 nullptr);
+                                 sQ, nullptr);
     else
         attend16<T, false, W, QB>(q + base, k + base, v + base, o + base, R, L, L, c, g, G, sK,
-                                  sV, nullptr);
+                                  sV, sQ, nullptr);
 }
 
 __global__ __launch_bounds__(kThreads) void attn_fwd32(const float *__restrict__ q,
@@ -807,6 +863,7 @@ __global__ __launch_bounds__(64 * W, QB == 1 ? 4 : 3) void fused16(const uint16_
                                                      int H, int G, int pad, float c) {
     __shared__ __attribute__((aligned(16))) uint16_t sK[2 * kKC * 64];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2 * kD * 64];
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[QB == 2 ? 16 * W * QB * kD : 8];
     __shared__ int16_t pos[kMaxFusedN];
     __shared__ uint64_t keep_bits[kMaxFusedN / 64];
     int b, h, g;
@@ -835,10 +892,10 @@ __global__ __launch_bounds__(64 * W, QB == 1 ? 4 : 3) void fused16(const uint16_
         if (run) {
             if (c > 0.f)
                 attend16<T, true, W, QB>(q + head0, k + head0, v + head0, out_head, R, L, Lp, c, gg, GG,
-                                     sK, sV, cls_dst);
+                                     sK, sV, sQ, cls_dst);
             else
                 attend16<T, false, W, QB>(q + head0, k + head0, v + head0, out_head, R, L, Lp, c, gg, GG,
-                                      sK, sV, cls_dst);
+                                      sK, sV, sQ, cls_dst);
         }
     }
     // zeros for the pruned rows: by the last workgroup of the head, after its
@@ -903,10 +960,8 @@ void launch_fwd16(const AttnArgs &a, float c, hipStream_t s) {
 template <typename T>
 void launch_fwd16_shape(const AttnArgs &a, float c, hipStream_t s) {
     const Shape sh = shape_for(a.max_seqlen);
-    if (sh.W == 4 && sh.QB == 1) launch_fwd16<T, 4, 1>(a, c, s);
-    else if (sh.W == 4) launch_fwd16<T, 4, 2>(a, c, s);
-    else if (sh.QB == 1) launch_fwd16<T, 8, 1>(a, c, s);
-    else launch_fwd16<T, 8, 2>(a, c, s);
+    if (sh.QB == 1) launch_fwd16<T, 4, 1>(a, c, s);
+    else launch_fwd16<T, 4, 2>(a, c, s);
 }
 
 template <typename T, int W, int QB>
@@ -923,10 +978,8 @@ template <typename T>
 void launch_fused16_shape(const FusedArgs &a, float c, hipStream_t s) {
     // the CLS-only mode computes one tile per head: the smallest workgroup
     const Shape sh = a.out ? shape_for(std::min(a.max_seqlen, a.N)) : Shape{4, 1};
-    if (sh.W == 4 && sh.QB == 1) launch_fused16<T, 4, 1>(a, c, s);
-    else if (sh.W == 4) launch_fused16<T, 4, 2>(a, c, s);
-    else if (sh.QB == 1) launch_fused16<T, 8, 1>(a, c, s);
-    else launch_fused16<T, 8, 2>(a, c, s);
+    if (sh.QB == 1) launch_fused16<T, 4, 1>(a, c, s);
+    else launch_fused16<T, 4, 2>(a, c, s);
 }
 
 }  // namespace

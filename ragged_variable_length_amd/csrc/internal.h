@@ -133,7 +133,7 @@ struct FusedArgs {
 
 // Longest padded sequence the fused kernel accepts: its workgroups keep the
 // image's kept positions as an int16 list in LDS (2048 entries = 4 KiB, which
-// keeps the workgroup within 40 KiB so four fit on one CU).
+// keeps the 64-row-tile workgroup within 40 KiB so four fit on one CU).
 constexpr int kMaxFusedN = 2048;
 
 // Packs with a single launch when B*N is at most this many tokens (each
