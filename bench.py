@@ -456,11 +456,21 @@ def region_time_us(r: Resident, launches: int) -> float:
     return e0.elapsed_time(e1) * 1000.0 / launches
 
 
+def evict_caches(flush_buf) -> None:
+    """Evict the L2s and the 256 MB MALL before a cold launch: a 512 MB write,
+    then a read of the same buffer.  The read writes the dirty lines of the
+    write back to HBM before the measured launch starts; after a write alone,
+    that write-back lands inside the next launch and adds 12-16 us at 384 px,
+    while a read alone, or the write and the read, give the same times."""
+    flush_buf.zero_()
+    flush_buf.view(torch.float32).sum()
+
+
 def kernel_time_us(r: Resident, launches: int, cold: bool, flush_buf=None,
                    cold_launches: int = 50) -> float:
     """Warm: region average of back-to-back launches.  Cold: median of single
-    launches between HIP events, each after a 512 MB write that evicts the
-    MALL (the events add about 2 us to each)."""
+    launches between HIP events, each after `evict_caches` (the events add
+    about 2 us to each)."""
     if not cold:
         return region_time_us(r, launches)
     r.step()
@@ -468,7 +478,7 @@ def kernel_time_us(r: Resident, launches: int, cold: bool, flush_buf=None,
     times = []
     for _ in range(cold_launches):
         if cold:
-            flush_buf.zero_()  # evict the 256 MB MALL between launches
+            evict_caches(flush_buf)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(r.stream)
@@ -484,15 +494,14 @@ def forward_alone(w, stream, launches: int, flush_buf, cold_launches: int) -> di
     """rattn_forward alone on the flat buffers of a workload (prepared on the
     host, resident in HBM), against its own algorithmic bytes (q, k, v read and
     o written once): warm, back-to-back region average from C++; cold, median
-    of single launches between HIP events, each after a 512 MB write that
-    evicts the MALL."""
+    of single launches between HIP events, each after `evict_caches`."""
     f = FlatResident(w, stream)
     step = f.c_step()
     lib = timing_lib()
     warm = c_region_us(step, WHAT_FORWARD, launches, stream)
     times = []
     for _ in range(cold_launches):
-        flush_buf.zero_()
+        evict_caches(flush_buf)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -742,7 +751,7 @@ def main():
         del flush
         line["cold"] = {"us": round(cold, 2), "hbm_frac": round(nbytes / (cold * 1e-6) / 1e9 / HBM_PEAK_GBS, 5),
                         "from": "median of single launches between HIP events, each after a 512 MB write "
-                                "that evicts the 256 MB MALL"}
+                                "and a read of it that evict the L2s and the 256 MB MALL"}
         print(f"[bench] {w.name}: cold {cold:.2f} us per launch", flush=True)
         line["padded_comparator"] = padded_comparison(r, K)
         pc = line["padded_comparator"]
