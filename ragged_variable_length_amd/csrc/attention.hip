@@ -422,15 +422,9 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
                         for (int i = 0; i < 4; ++i)
                             if (16 * blk + 4 * grp + i >= valid) s[qb][blk][i] = -INFINITY;
             }
+            if constexpr (!kPos) {
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                if constexpr (kPos) {
-#pragma unroll
-                    for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            s[qb][blk][i] = fast_exp2(__builtin_fmaf(s[qb][blk][i], c, -mc[qb]));
-                } else {
+                for (int qb = 0; qb < QB; ++qb) {
                     // scale <= 0 (degenerate but valid): scale, then the
                     // exact running max (masked scores stay -inf)
                     float mxn = -INFINITY;
@@ -463,34 +457,86 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
             // group g addresses key 32*ks + 16*h + 4*g + r/4, dims 16*dt + 4*(r%4).
             // The row sums of the rounded P come from the same B operand
             // against an all-ones A operand.  Each V operand serves all QB
-            // query blocks.
+            // query blocks.  For scale > 0 the probabilities of each 32-key
+            // half are computed here, next to the MFMAs that consume them.
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 if (ks == 0 || valid_p > 32) {
-                    V8 b[QB];
+                    const int r0 = 32 * ks + vr, r1 = r0 + 16;
+                    const uint16_t *v0 = Vs + r0 * 64 + vhalf;
+                    const uint16_t *v1 = Vs + r1 * 64 + vhalf;
+                    auto expo = [&](int qb, int blk, int i0) {
 #pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) {
+                        for (int i = i0; i < i0 + 2; ++i)
+                            s[qb][blk][i] = fast_exp2(__builtin_fmaf(s[qb][blk][i], c, -mc[qb]));
+                    };
+                    auto pack_b = [&](int qb) {
                         u32x4 pb;
                         pb[0] = pack2<T>(s[qb][2 * ks][0], s[qb][2 * ks][1]);
                         pb[1] = pack2<T>(s[qb][2 * ks][2], s[qb][2 * ks][3]);
                         pb[2] = pack2<T>(s[qb][2 * ks + 1][0], s[qb][2 * ks + 1][1]);
                         pb[3] = pack2<T>(s[qb][2 * ks + 1][2], s[qb][2 * ks + 1][3]);
-                        b[qb] = __builtin_bit_cast(V8, pb);
+                        return __builtin_bit_cast(V8, pb);
+                    };
+                    if constexpr (kPos && QB == 2) {
+                        // Explicit order (the compiler otherwise issues every
+                        // exponential before the first MFMA, leaving the matrix
+                        // pipe idle): the half's V^T operands first, then block
+                        // 0's probabilities, then each of block 0's MFMAs
+                        // followed by a quarter of block 1's exponentials, which
+                        // run while the MFMA does.
+                        u32x4 va[4];
+#pragma unroll
+                        for (int dt = 0; dt < 4; ++dt) {
+                            const u32x2 lo = lds_read_tr(v0 + 8 * vpiece(r0, 2 * dt + vp));
+                            const u32x2 hi = lds_read_tr(v1 + 8 * vpiece(r1, 2 * dt + vp));
+                            va[dt] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                        }
+#pragma unroll
+                        for (int blk = 2 * ks; blk < 2 * ks + 2; ++blk) {
+                            expo(0, blk, 0);
+                            expo(0, blk, 2);
+                        }
+                        const V8 b0 = pack_b(0);
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int dt = 0; dt < 4; ++dt) {
+                            acc[0][dt] = Mma<T>::run(__builtin_bit_cast(V8, va[dt]), b0, acc[0][dt]);
+                            expo(1, 2 * ks + (dt >> 1), 2 * (dt & 1));
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                        accl[0] = Mma<T>::run(ones, b0, accl[0]);
+                        const V8 b1 = pack_b(1);
+                        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                        for (int dt = 0; dt < 4; ++dt)
+                            acc[1][dt] = Mma<T>::run(__builtin_bit_cast(V8, va[dt]), b1, acc[1][dt]);
+                        accl[1] = Mma<T>::run(ones, b1, accl[1]);
+                    } else {
+                        if constexpr (kPos) {
+#pragma unroll
+                            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                                for (int blk = 2 * ks; blk < 2 * ks + 2; ++blk) {
+                                    expo(qb, blk, 0);
+                                    expo(qb, blk, 2);
+                                }
+                        }
+                        V8 b[QB];
+#pragma unroll
+                        for (int qb = 0; qb < QB; ++qb) b[qb] = pack_b(qb);
+#pragma unroll
+                        for (int dt = 0; dt < 4; ++dt) {
+                            const u32x2 lo = lds_read_tr(v0 + 8 * vpiece(r0, 2 * dt + vp));
+                            const u32x2 hi = lds_read_tr(v1 + 8 * vpiece(r1, 2 * dt + vp));
+                            const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+                            for (int qb = 0; qb < QB; ++qb)
+                                acc[qb][dt] = Mma<T>::run(__builtin_bit_cast(V8, a), b[qb], acc[qb][dt]);
+                        }
+#pragma unroll
+                        for (int qb = 0; qb < QB; ++qb) accl[qb] = Mma<T>::run(ones, b[qb], accl[qb]);
                     }
-                    const int r0 = 32 * ks + vr, r1 = r0 + 16;
-                    const uint16_t *v0 = Vs + r0 * 64 + vhalf;
-                    const uint16_t *v1 = Vs + r1 * 64 + vhalf;
-#pragma unroll
-                    for (int dt = 0; dt < 4; ++dt) {
-                        const u32x2 lo = lds_read_tr(v0 + 8 * vpiece(r0, 2 * dt + vp));
-                        const u32x2 hi = lds_read_tr(v1 + 8 * vpiece(r1, 2 * dt + vp));
-                        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-                        for (int qb = 0; qb < QB; ++qb)
-                            acc[qb][dt] = Mma<T>::run(__builtin_bit_cast(V8, a), b[qb], acc[qb][dt]);
-                    }
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) accl[qb] = Mma<T>::run(ones, b[qb], accl[qb]);
                 }
             }
         }

@@ -179,3 +179,4 @@ inline emu_s16x4 emu_ds_read_tr16(const void *p) {
 }
 #define __builtin_amdgcn_ds_read_tr16_b64_v4i16(P) emu_ds_read_tr16((const void *)(P))
 #define __builtin_amdgcn_s_waitcnt(X) ((void)0)
+#define __builtin_amdgcn_sched_barrier(X) ((void)0)
