@@ -258,6 +258,15 @@ def test_forward_unusual_scales(scale):
                           name=f"fwd_scale_{scale}"), flat=False)
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.125, 0.5])
+def test_forward_unusual_scales_two_block_tiles(scale):
+    # 300 positions select the 128-row tiles whose Q rows are staged in LDS;
+    # 32 x 8 = 256 heads give one workgroup per head, so each copies the next
+    # tile's Q rows while its current tile finishes
+    full(workloads.custom(32, 300, 8, "bf16", p_keep=0.9, seed=19, scale=scale,
+                          name=f"fwd_scale_{scale}_128_row_tiles"), flat=False)
+
+
 def test_forward_side_stream():
     w = workloads.deit_b_sweep(2, 0.8)
     s = torch.cuda.Stream()
