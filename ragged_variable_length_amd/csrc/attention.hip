@@ -197,7 +197,8 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
                                          uint16_t *sQ, uint16_t *__restrict__ cls_dst) {
     // Lp >= L is the length processed: L for ragged attention; for the padded
     // comparator, the padded length, whose extra keys are masked and whose
-    // extra query rows are computed on zeros and discarded
+    // extra query rows are computed (on zeros, or with two blocks per
+    // wavefront on copies of the last row) and discarded
     typedef typename Mma<T>::v8 V8;
     constexpr uint32_t kOneBits = Mma<T>::kOnePair;
     const int lane = threadIdx.x & 63;
