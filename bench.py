@@ -187,6 +187,12 @@ class BenchStats(ctypes.Structure):
         return {k: round(getattr(self, k), 2) for k, _ in self._fields_}
 
 
+class BenchPeaks(ctypes.Structure):
+    """bench_peaks_result of bench_peaks.hip."""
+    _fields_ = [("mfma_bf16_tflops", ctypes.c_double), ("fma_exp_per_s", ctypes.c_double),
+                ("exp_per_s", ctypes.c_double), ("fma_f32_tflops", ctypes.c_double)]
+
+
 class BenchStep(ctypes.Structure):
     _fields_ = [("src", ctypes.c_void_p * 3), ("packed", ctypes.c_void_p * 3),
                 ("o", ctypes.c_void_p), ("out_padded", ctypes.c_void_p),
@@ -225,8 +231,9 @@ def timing_lib():
         lib.bench_enqueue_cost.argtypes = [step, i32, i32, stats]
         lib.bench_graph_floor.argtypes = [step, i32, i32, i32, stats]
         lib.bench_loop.argtypes = [step, i32, i32]
+        lib.bench_peaks.argtypes = [i32, i32, P, ctypes.POINTER(BenchPeaks)]
         for f in (lib.bench_empty_floor, lib.bench_call_floor, lib.bench_enqueue_cost,
-                  lib.bench_graph_floor, lib.bench_loop):
+                  lib.bench_graph_floor, lib.bench_loop, lib.bench_peaks):
             f.restype = i32
         _timing = lib
     return _timing
@@ -546,7 +553,7 @@ def padded_comparison(r: Resident, launches: int, rounds: int = 3) -> dict:
     return out
 
 
-def large_configs(stream, launches: int, cold_launches: int) -> dict:
+def large_configs(stream, launches: int, cold_launches: int, box_gbs=None, peaks=None) -> dict:
     out = {}
     flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device="cuda")
     for name, maker in (("deit_b_384_50pct", workloads.deit_b_384),
@@ -557,7 +564,8 @@ def large_configs(stream, launches: int, cold_launches: int) -> dict:
         flops = attention_flops(r.lengths, w.H)
         row = {"B": w.B, "N": w.N, "H": w.H, "dtype": w.dtype, "T": r.T,
                "fused_bytes": nbytes, "attn_flops": flops,
-               "traffic_bytes": measured_traffic(w.name)}
+               "traffic_bytes": measured_traffic(w.name),
+               "roofs_us": roofs_us(nbytes, flops, box_gbs, peaks)}
         row["padded_comparator"] = padded_comparison(r, launches)
         row["three_call_and_stacks"] = three_call_and_stacks(r, launches)
         row["forward_alone"] = forward_alone(w, stream, launches, flush, cold_launches)
@@ -615,6 +623,40 @@ def box_copy_bandwidth(stream, nbytes: int = 1 << 30, reps: int = 10) -> float:
     sec = e0.elapsed_time(e1) / 1000.0 / reps
     del a, b
     return round(2 * nbytes / sec / 1e9, 1)
+
+
+def box_peaks(stream, grid: int = 1024, iters: int = 2048) -> dict:
+    """Box-measured compute ceilings (bench_peaks.hip, 1024 workgroups of 256
+    threads, eight independent chains per lane): dense bf16 MFMA, the
+    softmax's per-score pair (one fma feeding one exp2), exp2 alone and float32
+    fma -- next to the datasheet peaks the roofline fractions use."""
+    res = BenchPeaks()
+    if timing_lib().bench_peaks(grid, iters, stream.cuda_stream, ctypes.byref(res)) != 0:
+        raise RuntimeError("bench_peaks failed")
+    return {"mfma_bf16_TFLOPs": round(res.mfma_bf16_tflops, 1),
+            "fma_exp2_per_s": float(f"{res.fma_exp_per_s:.4g}"),
+            "exp2_per_s": float(f"{res.exp_per_s:.4g}"),
+            "fma_f32_TFLOPs": round(res.fma_f32_tflops, 1),
+            "from": "bench_peaks.hip: 1024 workgroups x 256 threads, 2048 iterations of eight "
+                    "independent chains per lane, HIP events around one launch after a warm-up"}
+
+
+def roofs_us(nbytes: int, flops: int, box_gbs, peaks) -> dict:
+    """Lower bounds on one launch of the attention path, us: its algorithmic
+    bytes at the HBM peak, its contraction flops at the dense MFMA peak, and
+    its H * sum(L^2) scores at the box's rate for one fma + one exp2 each (the
+    vector work every score needs at least; the kernel spends about four more
+    VALU instructions per score).  Datasheet peaks, and box-measured ones when
+    given."""
+    scores = flops // (4 * 64)
+    out = {"hbm": round(nbytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
+           "mfma": round(flops / (MFMA_PEAK_TFLOPS["bf16"] * 1e12) * 1e6, 2)}
+    if box_gbs:
+        out["hbm_box"] = round(nbytes / (box_gbs * 1e9) * 1e6, 2)
+    if peaks:
+        out["mfma_box"] = round(flops / (peaks["mfma_bf16_TFLOPs"] * 1e12) * 1e6, 2)
+        out["fma_exp2_box"] = round(scores / peaks["fma_exp2_per_s"] * 1e6, 2)
+    return out
 
 
 def tiny_fp32(stream, launches: int) -> dict:
@@ -746,6 +788,12 @@ def main():
         roofline["box_peak_from"] = "1 GiB device-to-device copy, read + written bytes / time"
         roofline["box_frac"] = round(achieved / box, 5)
         print(f"[bench] box-measured copy bandwidth {box} GB/s", flush=True)
+        peaks = box_peaks(stream)
+        line["box_peaks"] = peaks
+        print(f"[bench] box-measured peaks: bf16 MFMA {peaks['mfma_bf16_TFLOPs']} TFLOP/s, "
+              f"fma+exp2 {peaks['fma_exp2_per_s']:.3g}/s, exp2 {peaks['exp2_per_s']:.3g}/s, "
+              f"fp32 fma {peaks['fma_f32_TFLOPs']} TFLOP/s", flush=True)
+        line["roofs_us"] = roofs_us(nbytes, line["attn_flops"], box, peaks)
         flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device="cuda")
         cold = kernel_time_us(r, K, True, flush, cold_launches=200)
         del flush
@@ -761,7 +809,8 @@ def main():
         _print_stacks(w.name, line["three_call_and_stacks"])
         side = torch.cuda.Stream()  # graph capture needs a non-default stream
         line["dispatch_floor"] = dispatch_floors(side, iters=1000, warmup=100)
-        line["large_configs"] = large_configs(stream, launches=300, cold_launches=50)
+        line["large_configs"] = large_configs(stream, launches=300, cold_launches=50,
+                                              box_gbs=box, peaks=peaks)
         line["tiny_fp32"] = tiny_fp32(stream, launches=2000)
     if not args.quick and not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

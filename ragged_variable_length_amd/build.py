@@ -15,7 +15,7 @@ LIB = os.path.join(HERE, "librattn.so")
 SOURCES = ["api.hip", "pack.hip", "attention.hip", "repack.hip"]
 # host-side timing loops used by bench.py (links librattn.so; not product ABI)
 BENCH_LIB = os.path.join(HERE, "librattn_bench.so")
-BENCH_SOURCES = ["bench_host.hip"]
+BENCH_SOURCES = ["bench_host.hip", "bench_peaks.hip"]
 # CPython extension the Python binding calls (argument marshalling, links librattn.so)
 EXT = os.path.join(HERE, "_rattn" + sysconfig.get_config_var("EXT_SUFFIX"))
 EXT_SOURCE = "pymod.c"
