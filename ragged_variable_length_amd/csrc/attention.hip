@@ -288,13 +288,33 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
     const int ntile = (Lp + kQT16 - 1) / kQT16;
     if (g >= ntile) return;
     const bool resident = nch <= 2;
-    int t = g, ch = 0, step = 0;
+    // Chunk order: query rows of even 256-row blocks take the key chunks in
+    // order, those of odd blocks in reverse.  Where a workgroup's
+    // consecutive tiles cross such a boundary they meet at the same chunks:
+    // the last two chunks of one tile, still in the double buffer, are the
+    // first two of the next and are not copied again.  The order depends on
+    // a row's index only, so the results do not depend on the tile shape,
+    // the workgroups per head or the sequence bound.  The 64-row-tile shape
+    // serves bounds up to 256 only, where every row is in block 0, so it
+    // always runs in order.  Only the nreal chunks that hold kept keys are
+    // reversed: the padded comparator's all-masked chunks always come last,
+    // as in the ragged order, so that its bits stay those of the ragged
+    // kernel.  (A resident sequence has at most 128 rows, all in order.)
+    const int nreal = (L + kKC - 1) / kKC;
+    auto chunk_at = [&](int tile, int i) {
+        if constexpr (QB == 1) return i;
+        else return (i < nreal && (((tile * kQT16) >> 8) & 1)) ? nreal - 1 - i : i;
+    };
+    int t = g, idx = 0, step = 0;
+    int ch = chunk_at(t, 0);
+    int buf = resident ? ch : 0;
+    int held[2] = {ch, -1};  // the chunk each buffer holds (streamed sequences)
     u32x4 qf0[QB], qf1[QB], qn0[QB], qn1[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) qf0[qb] = qf1[qb] = qn0[qb] = qn1[qb] = zero4;
     if constexpr (kQL) stage_q(t);
     else load_q(t, qf0, qf1);
-    stage(0, 0);
+    stage(ch, buf);
     if (resident && nch == 2) {
         // both chunks in flight at once; wait for the Q rows and chunk 0
         // only (loads complete in issue order)
@@ -325,18 +345,31 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
     };
     reset();
     while (true) {
-        int nt = t, nc = ch + 1;
-        if (nc == nch) {
+        int nt = t, ni = idx + 1;
+        if (ni == nch) {
             nt = t + G;
-            nc = 0;
+            ni = 0;
         }
         const bool has_next = nt < ntile;
-        const bool next_tile = has_next && nc == 0;
-        const bool load_next = !resident && has_next;
-        if (load_next) stage(nc, (step + 1) & 1);
+        const bool next_tile = has_next && ni == 0;
+        // the next step's chunk: already in a buffer, or copied into the one
+        // this step does not read
+        const int nc = QB == 1 ? ni : (has_next ? chunk_at(nt, ni) : ch);
+        int nbuf = resident ? nc : (QB == 1 ? (step + 1) & 1 : buf ^ 1);
+        bool load_next = !resident && has_next;
+        if constexpr (QB == 2) {
+            if (load_next && held[buf] == nc) {
+                nbuf = buf;
+                load_next = false;
+            } else if (load_next && held[nbuf] == nc) {
+                load_next = false;
+            }
+            if (load_next) held[nbuf] = nc;
+        }
+        if (load_next) stage(nc, nbuf);
         if (!kQL && next_tile) load_q(nt, qn0, qn1);
 
-        const int buf = resident ? ch : (step & 1);
+        if constexpr (QB == 1) buf = resident ? ch : (step & 1);
         const uint16_t *Ks = sK + buf * (kKC * 64);
         const uint16_t *Vs = sV + buf * (kKC * 64);
         const int valid = L - ch * kKC;    // keys of this chunk inside the sequence
@@ -438,13 +471,17 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
                             mxn = fmaxf(mxn, x);
                         }
                     mxn = max_across_groups(mxn);
+                    // while every key so far is masked (a reversed tile of the
+                    // padded comparator can start with such a chunk) nothing
+                    // is rescaled and every probability is 0
                     const float mn = fmaxf(m[qb], mxn);
-                    const float alpha = fast_exp2(m[qb] - mn);
+                    const float alpha = m[qb] == mn ? 1.f : fast_exp2(m[qb] - mn);
+                    const float mref = mn == -INFINITY ? 0.f : mn;
                     m[qb] = mn;
 #pragma unroll
                     for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) s[qb][blk][i] = fast_exp2(s[qb][blk][i] - mn);
+                        for (int i = 0; i < 4; ++i) s[qb][blk][i] = fast_exp2(s[qb][blk][i] - mref);
 #pragma unroll
                     for (int dt = 0; dt < 4; ++dt) acc[qb][dt] *= alpha;
                     accl[qb][0] *= alpha;
@@ -542,7 +579,7 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
             }
         }
 
-        if (ch == nch - 1) {
+        if ((QB == 1 ? ch : idx) == nch - 1) {
             // tile t done: normalise and store; start the next tile afresh
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
@@ -586,7 +623,9 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
             }
         }
         t = nt;
+        idx = ni;
         ch = nc;
+        buf = nbuf;
         ++step;
     }
 }

@@ -148,6 +148,18 @@ def case_bounds():
     b = three_call(w)
     assert np.array_equal(U.bits(a["po"]), U.bits(b["po"])), "max_seqlen bound changed bits"
     print("max_seqlen exact / N / 4N: same bits", flush=True)
+    # N = 300 selects 128-row tiles, the exact bound (at most 256) 64-row
+    # tiles: rows past 128 take their key chunks in the same (reversed) order
+    # either way, so the bits agree
+    keep = _keep_lengths([240, 190, 131], 300, seed=56)
+    w = workloads.custom(3, 300, 1, "bf16", keep=keep, seed=57, name="bounds_shapes")
+    a = three_call(w, max_seqlen=max(w.kept_counts))
+    b = three_call(w)
+    assert np.array_equal(U.bits(a["po"]), U.bits(b["po"])), "tile shape changed bits"
+    fa, _ = fused(w, max_seqlen=max(w.kept_counts))
+    fb, _ = fused(w)
+    assert np.array_equal(U.bits(fa), U.bits(fb)), "tile shape changed fused bits"
+    print("max_seqlen 240 (64-row tiles) / 300 (128-row tiles): same bits", flush=True)
 
 
 def case_padded():
@@ -162,6 +174,22 @@ def case_padded():
             cls = torch.empty((w.B, w.H, w.D), dtype=w.q.dtype)
             for t in (out, cls):
                 t.view(torch.uint8).fill_(POISON)
+            rv.rattn_fused_padded(w.q, w.k, w.v, w.keep, w.scale, pad, out_padded=out, cls=cls)
+            assert np.array_equal(U.bits(out), U.bits(ref_out)), (w.name, pad, "out")
+            assert np.array_equal(U.bits(cls), U.bits(ref_cls)), (w.name, pad, "cls")
+        print(f"{w.name}: padded to {max(w.kept_counts)} and to {w.N}: bits equal to ragged",
+              flush=True)
+    # 128-row tiles with rows past 128 (their key chunks run in reverse),
+    # padded to N: the all-masked chunks come after the reversed ones; the
+    # degenerate scales too
+    keep = _keep_lengths([1, 0, 17, 65, 200, 150], 300, seed=54)
+    for scale in (0.125, 0.0, -0.125):
+        w = workloads.custom(6, 300, 1, "bf16", keep=keep.clone(), seed=55, scale=scale,
+                             name=f"padded_reversed_{scale}")
+        ref_out, ref_cls = fused(w)
+        for pad in (max(w.kept_counts), w.N):
+            out = torch.empty_like(w.q)
+            cls = torch.empty((w.B, w.H, w.D), dtype=w.q.dtype)
             rv.rattn_fused_padded(w.q, w.k, w.v, w.keep, w.scale, pad, out_padded=out, cls=cls)
             assert np.array_equal(U.bits(out), U.bits(ref_out)), (w.name, pad, "out")
             assert np.array_equal(U.bits(cls), U.bits(ref_cls)), (w.name, pad, "cls")
