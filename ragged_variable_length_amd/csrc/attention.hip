@@ -789,11 +789,18 @@ __device__ __forceinline__ bool decode_group(int BH, int H, int G, int *b, int *
 // One workgroup per (image, head) when the batch has at least as many heads
 // as the chip has CUs; otherwise each head's query tiles (16*W rows) are
 // dealt to G workgroups (tiles g, g+G, ...), G = CUs / heads, at most one per
-// tile.  Splitting further only adds workgroups that re-rank the image and
-// re-stream the head's K/V rows.  In the fused kernel the last workgroup of
-// each head writes the pruned rows' zeros; while the chip has room
-// (`spare_for_zeros`) a head gets at least two workgroups so that those
-// stores overlap the attention of the first.
+// tile.  In the fused kernel splitting further only adds workgroups that
+// re-rank the image (384 px, three workgroups per head: 47.3 -> 50.3 us).
+// The last of a head's workgroups writes the pruned rows' zeros; while the
+// chip has room (`spare_for_zeros`) a head gets at least two workgroups so
+// that those stores overlap the attention of the first.  The flat kernel has
+// no ranking to repeat: with 128-row tiles its heads are dealt to up to three
+// workgroups, whose copies of each K/V chunk, made at about the same time on
+// one XCD, share its L2, and the smaller units even out the load over the
+// dispatch rounds (384 px: 41.3 -> 39.0 us; four or five workgroups per head
+// were slower, 51.9 and 39.8 us).  With 64-row tiles (bounds up to 256) it
+// keeps the plain rule: at batch 512 four workgroups per head took 37.4 ->
+// 60.3 us.
 constexpr int64_t kComputeUnits = 256;
 
 int tile_groups(int B, int H, int max_seqlen, int rows, bool spare_for_zeros) {
@@ -801,6 +808,7 @@ int tile_groups(int B, int H, int max_seqlen, int rows, bool spare_for_zeros) {
     const int64_t pairs = std::max<int64_t>((int64_t)B * H, 1);
     int64_t G = kComputeUnits / pairs;
     if (spare_for_zeros && pairs < kComputeUnits) G = std::max<int64_t>(G, 2);
+    if (!spare_for_zeros && rows == 128) G = std::max<int64_t>(G, std::min(ntiles, 3));
     return (int)std::max<int64_t>(1, std::min<int64_t>(G, std::max(ntiles, spare_for_zeros ? 2 : 1)));
 }
 
