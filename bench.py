@@ -27,6 +27,7 @@ import ctypes
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -328,21 +329,37 @@ class StackResident:
         return s
 
 
-def c_region_us(step: BenchStep, what: int, reps: int, stream) -> float:
-    """Average device time of one `what` step: `reps` steps enqueued back to
-    back from C++, HIP events on the launch stream at the two ends only."""
-    lib = timing_lib()
-    if lib.bench_loop(ctypes.byref(step), what, 3) != 0:
-        raise RuntimeError(f"bench_loop({what}) failed")
+def settled_region_us(enqueue, stream, reps: int, rounds: int = 3) -> float:
+    """Average device time of one step, `enqueue(n)` putting n steps on
+    `stream` back to back: an untimed warm-up of 2*reps steps (at least 200),
+    then `rounds` regions of `reps` steps with HIP events on the launch stream
+    at their two ends only, and the median region.  The GPU takes a few tens
+    of ms under load to settle: after a three-step warm-up the first
+    300-launch region of rattn_forward at 384 px ran 44.2 us, the next ones
+    41.0 and 38.9-39.2."""
+    enqueue(max(2 * reps, 200))
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    if lib.bench_loop(ctypes.byref(step), what, reps) != 0:
-        raise RuntimeError(f"bench_loop({what}) failed")
-    e1.record(stream)
-    e1.synchronize()
-    return e0.elapsed_time(e1) * 1000.0 / reps
+    times = []
+    for _ in range(rounds):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        enqueue(reps)
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1) * 1000.0 / reps)
+    return statistics.median(times)
+
+
+def c_region_us(step: BenchStep, what: int, reps: int, stream) -> float:
+    """Average device time of one `what` step, enqueued back to back from C++
+    (settled_region_us)."""
+    lib = timing_lib()
+
+    def enqueue(n):
+        if lib.bench_loop(ctypes.byref(step), what, n) != 0:
+            raise RuntimeError(f"bench_loop({what}) failed")
+    return settled_region_us(enqueue, stream, reps)
 
 
 def three_call_and_stacks(r: Resident, reps: int) -> dict:
@@ -447,20 +464,14 @@ def dispatch_floors(stream, iters: int, warmup: int) -> dict:
 
 
 def region_time_us(r: Resident, launches: int) -> float:
-    """Average rattn_fused duration over back-to-back launches: HIP events on
-    the launch stream at the two ends of the region only (an event between
-    launches adds a few microseconds of its own to each)."""
-    for _ in range(3):
-        r.step()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(r.stream)
-    for _ in range(launches):
-        r.step()
-    e1.record(r.stream)
-    e1.synchronize()
-    return e0.elapsed_time(e1) * 1000.0 / launches
+    """Average rattn_fused duration over back-to-back launches through the
+    Python binding (settled_region_us: HIP events at the two ends of each
+    region only; an event between launches adds a few microseconds of its
+    own to each)."""
+    def enqueue(n):
+        for _ in range(n):
+            r.step()
+    return settled_region_us(enqueue, r.stream, launches)
 
 
 def evict_caches(flush_buf) -> None:
