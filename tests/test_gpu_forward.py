@@ -214,6 +214,46 @@ def test_forward_max_seqlen_bound_does_not_change_bits():
     assert np.array_equal(bits(a), bits(b)) and np.array_equal(bits(a), bits(c))
 
 
+def _keep_with_lengths(B, N, lo, hi, seed):
+    """Keep mask whose image b keeps a random subset of lo..hi positions."""
+    g = torch.Generator().manual_seed(seed)
+    keep = torch.zeros((B, N), dtype=torch.uint8)
+    for b in range(B):
+        L = int(torch.randint(lo, hi + 1, (1,), generator=g))
+        keep[b, torch.randperm(N, generator=g)[:L]] = 1
+    return keep
+
+
+def test_forward_bound_across_tile_shapes_does_not_change_bits():
+    # N = 300 selects 128-row tiles (up to three workgroups per head); the
+    # exact bound (at most 250) selects 64-row tiles
+    w = workloads.custom(32, 300, 8, "bf16", keep=_keep_with_lengths(32, 300, 130, 250, 60),
+                         seed=61, name="fwd_bound_shapes")
+    flat_cu = host_flat(w)
+    say("max_seqlen exact (64-row tiles) vs N (128-row tiles)")
+    a, _ = run_forward(w, max_seqlen=max(w.kept_counts), flat_cu=flat_cu)
+    b, _ = run_forward(w, max_seqlen=w.N, flat_cu=flat_cu)
+    assert np.array_equal(bits(a), bits(b))
+
+
+def test_forward_batch_equals_images_one_by_one():
+    # rows past 256 take the key chunks in reverse; the batch and one image
+    # alone split the heads over workgroups differently.  Same bits.
+    w = workloads.custom(32, 400, 8, "bf16", keep=_keep_with_lengths(32, 400, 260, 380, 62),
+                         seed=63, name="fwd_batch_vs_single")
+    flat, cu = host_flat(w)
+    say("256-head batch vs images one by one, N=400, kept 260..380")
+    o, T = run_forward(w, flat_cu=(flat, cu))
+    for b in (0, 7, 31):
+        s, e = int(cu[b]), int(cu[b + 1])
+        one = workloads.custom(1, 400, 8, "bf16", keep=w.keep[b:b + 1].clone(), seed=63,
+                               name=f"fwd_single_{b}")
+        one.q, one.k, one.v = (t[b:b + 1].clone() for t in (w.q, w.k, w.v))
+        o1, T1 = run_forward(one)
+        assert T1 == e - s
+        assert np.array_equal(bits(o1[:T1]), bits(o[s:e])), b
+
+
 def test_forward_image_longer_than_bound_is_left_unwritten():
     lengths = [10, 40, 12]
     keep = _keep_with_lengths(lengths, 64, seed=18)

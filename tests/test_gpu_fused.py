@@ -198,6 +198,44 @@ def test_fused_max_seqlen_bound_does_not_change_bits():
         assert np.array_equal(bits(x[0]), bits(y[0])) and np.array_equal(bits(x[1]), bits(y[1]))
 
 
+def _keep_with_lengths(B, N, lo, hi, seed):
+    """Keep mask whose image b keeps a random subset of lo..hi positions."""
+    g = torch.Generator().manual_seed(seed)
+    keep = torch.zeros((B, N), dtype=torch.uint8)
+    for b in range(B):
+        L = int(torch.randint(lo, hi + 1, (1,), generator=g))
+        keep[b, torch.randperm(N, generator=g)[:L]] = 1
+    return keep
+
+
+def test_fused_bound_across_tile_shapes_does_not_change_bits():
+    # N = 300 selects 128-row tiles; the exact bound (at most 250) selects
+    # 64-row tiles
+    w = workloads.custom(32, 300, 8, "bf16", keep=_keep_with_lengths(32, 300, 130, 250, 60),
+                         seed=61, name="bound_shapes")
+    say("max_seqlen exact (64-row tiles) vs N (128-row tiles)")
+    a = run_fused(w, max_seqlen=max(w.kept_counts))
+    b = run_fused(w, max_seqlen=w.N)
+    assert np.array_equal(bits(a[0]), bits(b[0])) and np.array_equal(bits(a[1]), bits(b[1]))
+
+
+def test_fused_batch_equals_images_one_by_one():
+    # 256 heads: one workgroup per head, whose later tiles take the key
+    # chunks of rows past 256 in reverse and reuse the double buffer's chunks;
+    # one image alone: a workgroup per tile, no reuse.  Same bits.
+    w = workloads.custom(32, 400, 8, "bf16", keep=_keep_with_lengths(32, 400, 260, 380, 62),
+                         seed=63, name="batch_vs_single")
+    say("256-head batch vs images one by one, N=400, kept 260..380")
+    out, cls = run_fused(w)
+    for b in (0, 7, 31):
+        one = workloads.custom(1, 400, 8, "bf16", keep=w.keep[b:b + 1].clone(), seed=63,
+                               name=f"single_{b}")
+        one.q, one.k, one.v = (t[b:b + 1].clone() for t in (w.q, w.k, w.v))
+        o1, c1 = run_fused(one)
+        assert np.array_equal(bits(o1[0]), bits(out[b])), b
+        assert np.array_equal(bits(c1[0]), bits(cls[b])), b
+
+
 def test_fused_poisoned_pruned_rows_do_not_leak():
     w = workloads.deit_b_sweep(4, 0.5)
     say("NaN-poisoned pruned rows")
