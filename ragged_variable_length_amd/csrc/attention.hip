@@ -17,17 +17,20 @@
 //  * A workgroup is W wavefronts, each owning QB blocks of 16 query rows, so
 //    a query tile is 16*W*QB rows (4x1: 64 rows up to 256 positions, 4x2:
 //    128 rows beyond).  The query tiles of one (image, head) go to G
-//    workgroups (tiles g, g+G, ...); G > 1 only when the batch has fewer
-//    heads than the chip has CUs.  Workgroup ids are laid out so that the G
-//    workgroups of one (image, head) land on the same XCD (ids are dealt to
-//    the 8 XCDs round-robin), keeping that head's K/V rows in one L2.
+//    workgroups (tiles g, g+G, ...): G > 1 when the batch has fewer heads
+//    than the chip has CUs, and in the flat kernel with 128-row tiles (up to
+//    three per head).  Workgroup ids are laid out so that the G workgroups of
+//    one (image, head) land on the same XCD (ids are dealt to the 8 XCDs
+//    round-robin), keeping that head's K/V rows in one L2.
 //  * Keys stream through LDS in chunks of 64, double-buffered, copied by
 //    global->LDS DMA (global_load_lds_dwordx4, 16 bytes per lane straight
 //    into the lane's LDS slot).  The copy of the next step's chunk is in
 //    flight while the current one is computed, one barrier per step; a
-//    sequence of at most two chunks stays resident.  16-byte pieces of each
-//    K and V row are XOR-permuted so that the operand reads hit distinct
-//    banks without padding.
+//    sequence of at most two chunks stays resident.  Query rows of odd
+//    256-row blocks take the chunks in reverse, so that a workgroup's tile
+//    crossing such a boundary starts with the two chunks still in its
+//    buffers.  16-byte pieces of each K and V row are XOR-permuted so that
+//    the operand reads hit distinct banks without padding.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_16x16x32_{bf16,f16}: in the accumulator layout each lane holds
 //    4 keys of ONE query, so the running max and sum are per-lane scalars (the
