@@ -706,6 +706,43 @@ def cpu_baseline(w, budget_s: float) -> dict:
                       f"oracle's scan, pack, attention and unpack, {dt:.1f} s on 1 host thread"}
 
 
+def _oracle_batches(maker: str, budget_s: float) -> tuple:
+    """Worker of cpu_baseline_all_cores: the one-thread loop of cpu_baseline
+    on a workload rebuilt from its seed (workloads.by_name(maker)); returns
+    (batches, seconds)."""
+    import oracle  # test infrastructure; used only for this reported baseline
+    w = workloads.by_name(maker)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        res = oracle.pipeline(w)
+        oracle.unpack(res["o64"], w.keep, res["cu"])
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    return reps, time.perf_counter() - t0
+
+
+def cpu_baseline_all_cores(w, maker: str, budget_s: float, max_procs: int = 16) -> dict:
+    """The CPU oracle on every host core at once: one worker process per core
+    (at most max_procs, the host share of one GPU), each running the
+    one-thread loop of cpu_baseline for the budget; images per second summed
+    over the workers.  Workers are started fresh (spawn): none touches the
+    GPU."""
+    import concurrent.futures
+    import multiprocessing
+    procs = max(1, min(max_procs, os.cpu_count() or 1))
+    ctx = multiprocessing.get_context("spawn")
+    with concurrent.futures.ProcessPoolExecutor(max_workers=procs, mp_context=ctx) as ex:
+        runs = list(ex.map(_oracle_batches, [maker] * procs, [budget_s] * procs))
+    rate = sum(reps * w.B / dt for reps, dt in runs)
+    batches = sum(reps for reps, _ in runs)
+    return {"value": round(rate, 2), "unit": "seqs/s", "cores": procs, "kind": "oracle",
+            "sample": f"{batches} full batch(es) of the {w.name} workload (B={w.B}) through the "
+                      f"fp64 oracle's scan, pack, attention and unpack, {procs} worker "
+                      f"process(es) of one thread for {budget_s:.0f} s each"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -825,6 +862,7 @@ def main():
         line["tiny_fp32"] = tiny_fp32(stream, launches=2000)
     if not args.quick and not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        line["cpu_baseline_all_cores"] = cpu_baseline_all_cores(w, "deit_s", args.cpu_budget)
     print(json.dumps(line), flush=True)
 
 
