@@ -214,7 +214,7 @@ def test_forward_max_seqlen_bound_does_not_change_bits():
     assert np.array_equal(bits(a), bits(b)) and np.array_equal(bits(a), bits(c))
 
 
-def _keep_with_lengths(B, N, lo, hi, seed):
+def _keep_length_range(B, N, lo, hi, seed):
     """Keep mask whose image b keeps a random subset of lo..hi positions."""
     g = torch.Generator().manual_seed(seed)
     keep = torch.zeros((B, N), dtype=torch.uint8)
@@ -227,7 +227,7 @@ def _keep_with_lengths(B, N, lo, hi, seed):
 def test_forward_bound_across_tile_shapes_does_not_change_bits():
     # N = 300 selects 128-row tiles (up to three workgroups per head); the
     # exact bound (at most 250) selects 64-row tiles
-    w = workloads.custom(32, 300, 8, "bf16", keep=_keep_with_lengths(32, 300, 130, 250, 60),
+    w = workloads.custom(32, 300, 8, "bf16", keep=_keep_length_range(32, 300, 130, 250, 60),
                          seed=61, name="fwd_bound_shapes")
     flat_cu = host_flat(w)
     say("max_seqlen exact (64-row tiles) vs N (128-row tiles)")
@@ -239,7 +239,7 @@ def test_forward_bound_across_tile_shapes_does_not_change_bits():
 def test_forward_batch_equals_images_one_by_one():
     # rows past 256 take the key chunks in reverse; the batch and one image
     # alone split the heads over workgroups differently.  Same bits.
-    w = workloads.custom(32, 400, 8, "bf16", keep=_keep_with_lengths(32, 400, 260, 380, 62),
+    w = workloads.custom(32, 400, 8, "bf16", keep=_keep_length_range(32, 400, 260, 380, 62),
                          seed=63, name="fwd_batch_vs_single")
     flat, cu = host_flat(w)
     say("256-head batch vs images one by one, N=400, kept 260..380")

@@ -198,7 +198,7 @@ def test_fused_max_seqlen_bound_does_not_change_bits():
         assert np.array_equal(bits(x[0]), bits(y[0])) and np.array_equal(bits(x[1]), bits(y[1]))
 
 
-def _keep_with_lengths(B, N, lo, hi, seed):
+def _keep_length_range(B, N, lo, hi, seed):
     """Keep mask whose image b keeps a random subset of lo..hi positions."""
     g = torch.Generator().manual_seed(seed)
     keep = torch.zeros((B, N), dtype=torch.uint8)
@@ -211,7 +211,7 @@ def _keep_with_lengths(B, N, lo, hi, seed):
 def test_fused_bound_across_tile_shapes_does_not_change_bits():
     # N = 300 selects 128-row tiles; the exact bound (at most 250) selects
     # 64-row tiles
-    w = workloads.custom(32, 300, 8, "bf16", keep=_keep_with_lengths(32, 300, 130, 250, 60),
+    w = workloads.custom(32, 300, 8, "bf16", keep=_keep_length_range(32, 300, 130, 250, 60),
                          seed=61, name="bound_shapes")
     say("max_seqlen exact (64-row tiles) vs N (128-row tiles)")
     a = run_fused(w, max_seqlen=max(w.kept_counts))
@@ -223,7 +223,7 @@ def test_fused_batch_equals_images_one_by_one():
     # 256 heads: one workgroup per head, whose later tiles take the key
     # chunks of rows past 256 in reverse and reuse the double buffer's chunks;
     # one image alone: a workgroup per tile, no reuse.  Same bits.
-    w = workloads.custom(32, 400, 8, "bf16", keep=_keep_with_lengths(32, 400, 260, 380, 62),
+    w = workloads.custom(32, 400, 8, "bf16", keep=_keep_length_range(32, 400, 260, 380, 62),
                          seed=63, name="batch_vs_single")
     say("256-head batch vs images one by one, N=400, kept 260..380")
     out, cls = run_fused(w)
