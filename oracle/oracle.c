@@ -23,7 +23,7 @@
  *                pipeline is agnostic to the pruning method, including methods
  *                that prune again at later blocks.
  *
- * Readings where the pages leave a step open (listed in the design doc):
+ * Readings where the pages leave a step open:
  *   - keep mask is one byte per token, nonzero = kept;
  *   - cu_seqlens is int32 [B+1] with cu[0] = 0 (exclusive prefix sum);
  *   - inside the flat buffer, images are in ascending b and, within an image,
