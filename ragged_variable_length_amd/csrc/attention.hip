@@ -153,11 +153,16 @@ struct PaddedRows {
 // LDS tiles of the 16-bit path are 64 rows x 128 bytes, written by
 // global->LDS DMA (each lane's 16 bytes land at base + 16*lane) and read as
 // MFMA operands.  The 16-byte pieces of each row are XOR-permuted so that the
-// reads hit distinct banks: K rows (read as 16-byte row slices) by
-// (row ^ row>>3) & 7, V rows (read transposed, 8 bytes per lane) by
-// 2 * ((row ^ row>>1) & 3).  A lane fetches from global memory whichever piece
-// belongs in its LDS slot, so the permutation costs nothing at staging time.
-__device__ __forceinline__ int kpiece(int row, int p) { return p ^ ((row ^ (row >> 3)) & 7); }
+// reads hit distinct banks: K and Q rows (read as 16-byte row slices, one row
+// per lane of each group of 16) by (row >> 1) & 7, V rows (read transposed, 8
+// bytes per lane) by 2 * ((row ^ row>>1) & 3).  A lane fetches from global
+// memory whichever piece belongs in its LDS slot, so the permutation costs
+// nothing at staging time.  On gfx950 the K/Q permutation was chosen by the
+// LDS bank-conflict counter: (row ^ row>>3) & 7, which has no conflict if a
+// 16-byte read is served 8 or 16 consecutive lanes at a time, left 1.8e6
+// conflict cycles per 384-px forward launch (0.15e6 per operand read per
+// step); (row >> 1) & 7 leaves none and took that launch from 39.1 to 38.1 us.
+__device__ __forceinline__ int kpiece(int row, int p) { return p ^ ((row >> 1) & 7); }
 __device__ __forceinline__ int vpiece(int row, int p) { return p ^ (((row ^ (row >> 1)) & 3) << 1); }
 
 #define RATTN_LDS(p) ((__attribute__((address_space(3))) void *)(p))
