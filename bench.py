@@ -176,6 +176,20 @@ def pmc_target() -> None:
         del r
 
 
+def pmc_forward(name: str) -> None:
+    """Five rattn_forward launches on one workload's flat buffers, prepared on
+    the host (run under rocprofv3 --pmc for the SQ counters of the attention
+    loop)."""
+    rattn_init()
+    stream = torch.cuda.current_stream()
+    f = FlatResident(workloads.by_name(name), stream)
+    step = f.c_step()
+    if timing_lib().bench_loop(ctypes.byref(step), WHAT_FORWARD, 5) != 0:
+        raise RuntimeError("bench_loop(rattn_forward) failed")
+    torch.cuda.synchronize()
+    print(f"[pmc] {f.w.name}: rattn_forward x5", flush=True)
+
+
 # ---------------------------------------------------------------------------
 # C++ timing helper (host clock around call + sync; no interpreter in the loop)
 # ---------------------------------------------------------------------------
@@ -754,6 +768,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-target", action="store_true",
                     help="only the launches the traffic counters are read on, then exit")
+    ap.add_argument("--pmc-forward", choices=["deit_s", "deit_b_384", "large_batch"],
+                    help="only five rattn_forward launches on one workload (for the SQ "
+                         "counters of the attention loop), then exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the traffic summary of two counter runs, then exit")
     ap.add_argument("--stack-only", choices=sorted(STACK_WORKLOADS),
@@ -765,7 +782,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the path has no "
-              "cross-GPU step and this build runs on a single MI355X; use --gpus 1.",
+              "cross-GPU step and the library runs on a single MI355X; use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
@@ -773,6 +790,9 @@ def main():
         sys.exit(1)
     if args.pmc_target:
         pmc_target()
+        return
+    if args.pmc_forward:
+        pmc_forward(args.pmc_forward)
         return
     if args.stack_only:
         rattn_init()
