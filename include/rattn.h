@@ -44,9 +44,12 @@
  *   - Contract the host cannot check without a device round trip: cu_seqlens
  *     must agree with the buffers' capacities, and max_seqlen must be >= every
  *     image's kept count.  Any such upper bound (N always is one) gives
- *     bitwise-identical results.
+ *     bitwise-identical results.  The opt-in debug-validate mode
+ *     (rattn_set_validate) checks the bound and the shape of cu_seqlens with a
+ *     device-to-host read before launching.
  *   - Thread safety: entry points may be called from several threads; the
- *     only global state is the one-time device check of rattn_init.
+ *     only global state is the one-time device check of rattn_init and the
+ *     debug-validate flag.
  */
 #ifndef RATTN_H
 #define RATTN_H
@@ -91,6 +94,34 @@ const char *rattn_status_string(rattn_status s);
 int rattn_version(void);
 
 /*
+ * rattn_set_validate -- opt-in debug-validate mode for the contract a call
+ * cannot check from its host arguments alone ([FA2]: the flat buffer and its
+ * cumulative lengths are only as good as the caller's bookkeeping).
+ *
+ *   on          nonzero switches the mode on for the whole process, 0 off
+ *               (the default).  Returns the previous setting (0 or 1).
+ *
+ * In the mode, after the host checks and before any launch, an entry point
+ * copies what it needs to host memory, ordered after the earlier work on its
+ * stream, waits for it, and returns RATTN_ERR_INVALID_ARG with nothing
+ * launched when:
+ *   rattn_forward       cu_seqlens[0] != 0, cu_seqlens decreases, or an image
+ *                       has more rows than max_seqlen;
+ *   rattn_fused         an image keeps more tokens than max_seqlen;
+ *   rattn_fused_padded  an image keeps more tokens than pad_len;
+ *   rattn_unpack        cu_seqlens is not the prefix sum of keep's counts;
+ *   rattn_repack        cu_seqlens[0] != 0 or cu_seqlens decreases.
+ * A failed copy or wait returns RATTN_ERR_HIP.  The mode makes those calls
+ * synchronous and costs a device-to-host round trip each: it is for
+ * debugging, and cannot be used under stream capture.  rattn_pack computes
+ * cu_seqlens itself and is unaffected.  Thread-safe (an atomic flag).
+ */
+int rattn_set_validate(int on);
+
+/* Current debug-validate setting: 1 on, 0 off. */
+int rattn_get_validate(void);
+
+/*
  * rattn_pack -- [Pipeline] steps 1 and 2: cu_seqlens and the coalesced pack.
  *
  *   src[i]      device, [B, N, row_elems] elements of `dt` (padded input i)
@@ -130,7 +161,9 @@ rattn_status rattn_pack(const void *const *src, void *const *dst, int n_tensors,
  *   max_seqlen  host upper bound on every kept count (>= 0; 0 = nothing to do;
  *               max_seqlen * H * head_dim * element size must not exceed
  *               RATTN_MAX_IMAGE_BYTES).  An image whose kept count exceeds it
- *               breaks the contract; its output rows are left unwritten.
+ *               breaks the contract: its output rows are left unwritten, or,
+ *               in debug-validate mode, the call returns
+ *               RATTN_ERR_INVALID_ARG before launching.
  *   H           heads (>= 1);  head_dim must be RATTN_HEAD_DIM
  *   scale       finite float multiplying the dot products (1/sqrt(64) for ViT)
  * Arithmetic: q.k and p.v contractions on the matrix cores with float32

@@ -9,10 +9,10 @@ torch) for repeated calls of the three, and `FusedPlan` is a rattn_fused call
 whose arguments are checked and marshalled once.
 """
 from ._binding import (LIB_PATH, RattnError, load, rattn_forward, rattn_fused,
-                       rattn_fused_padded, rattn_init, rattn_pack, rattn_repack, rattn_unpack,
-                       status_string)
+                       rattn_fused_padded, rattn_get_validate, rattn_init, rattn_pack,
+                       rattn_repack, rattn_set_validate, rattn_unpack, status_string)
 from .pipeline import FusedPlan, RaggedPipeline
 
 __all__ = ["LIB_PATH", "FusedPlan", "RattnError", "RaggedPipeline", "load", "rattn_forward",
-           "rattn_fused", "rattn_fused_padded", "rattn_init", "rattn_pack", "rattn_repack",
-           "rattn_unpack", "status_string"]
+           "rattn_fused", "rattn_fused_padded", "rattn_get_validate", "rattn_init", "rattn_pack",
+           "rattn_repack", "rattn_set_validate", "rattn_unpack", "status_string"]

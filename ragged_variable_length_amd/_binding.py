@@ -49,6 +49,10 @@ def load() -> ctypes.CDLL:
     lib.rattn_status_string.restype = ctypes.c_char_p
     lib.rattn_version.argtypes = []
     lib.rattn_version.restype = i32
+    lib.rattn_set_validate.argtypes = [i32]
+    lib.rattn_set_validate.restype = i32
+    lib.rattn_get_validate.argtypes = []
+    lib.rattn_get_validate.restype = i32
     lib.rattn_pack.argtypes = [P, P, i32, P, i32, i32, i32, i32, P, P, P, P]
     lib.rattn_pack.restype = i32
     lib.rattn_forward.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f32, i32, P]
@@ -128,6 +132,17 @@ def _check(fn: str, status: int) -> None:
 
 def rattn_init() -> None:
     _check("rattn_init", ext().init())
+
+
+def rattn_set_validate(on: bool) -> bool:
+    """Switch the library's debug-validate mode on or off for the process;
+    returns the previous setting (C: rattn_set_validate)."""
+    return bool(ext().set_validate(1 if on else 0))
+
+
+def rattn_get_validate() -> bool:
+    """Whether debug-validate mode is on (C: rattn_get_validate)."""
+    return bool(ext().get_validate())
 
 
 def rattn_pack(srcs, dsts, keep: torch.Tensor, cu_seqlens: torch.Tensor,

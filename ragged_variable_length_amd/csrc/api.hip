@@ -7,9 +7,14 @@
 // kernel that writes its arguments straight into the launch): plain-int
 // argument checks, one kernel-argument struct built on the stack, one launch
 // per kernel, no allocation, no device-to-host traffic, no synchronisation.
+// The one exception is the debug-validate mode a caller may switch on
+// (rattn_set_validate), which reads the kept counts back to check the
+// contract before launching.
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "internal.h"
 #include "rattn.h"
@@ -20,6 +25,8 @@ namespace {
 
 std::once_flag g_once;
 rattn_status g_init = RATTN_ERR_NO_DEVICE;
+// debug-validate mode (rattn_set_validate): off unless a caller opts in
+std::atomic<int> g_validate{0};
 
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 inline bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
@@ -44,6 +51,76 @@ inline int row_vectors(int row_elems, rattn_dtype dt) {
     const int64_t bytes = (int64_t)row_elems * es;
     if (bytes % 16 != 0 || bytes / 16 > (1 << 24)) return 0;
     return (int)(bytes / 16);
+}
+
+// ---------------------------------------------------------------------------
+// debug-validate mode: the parts of the contract the host cannot see without
+// reading device memory.  Each check copies what it needs to host memory,
+// ordered after the earlier work on the caller's stream, and waits for it.
+// ---------------------------------------------------------------------------
+inline bool validating() { return g_validate.load(std::memory_order_relaxed) != 0; }
+
+rattn_status read_back(void *host, const void *dev, size_t n, hipStream_t s) {
+    if (n == 0) return RATTN_OK;
+    if (hipMemcpyAsync(host, dev, n, hipMemcpyDeviceToHost, s) != hipSuccess) return RATTN_ERR_HIP;
+    return hipStreamSynchronize(s) == hipSuccess ? RATTN_OK : RATTN_ERR_HIP;
+}
+
+// cu_seqlens must start at 0 and never decrease; *longest = its largest step.
+rattn_status validate_cu(const int32_t *cu_dev, int B, hipStream_t s, std::vector<int32_t> &cu,
+                         int *longest) {
+    cu.assign((size_t)B + 1, 0);
+    rattn_status st = read_back(cu.data(), cu_dev, cu.size() * sizeof(int32_t), s);
+    if (st != RATTN_OK) return st;
+    if (cu[0] != 0) return RATTN_ERR_INVALID_ARG;
+    int m = 0;
+    for (int b = 0; b < B; ++b) {
+        const int64_t d = (int64_t)cu[b + 1] - cu[b];
+        if (d < 0) return RATTN_ERR_INVALID_ARG;
+        if (d > m) m = (int)d;
+    }
+    *longest = m;
+    return RATTN_OK;
+}
+
+// Kept count of every image of a [B, N] mask.
+rattn_status kept_counts(const uint8_t *keep_dev, int B, int N, hipStream_t s,
+                         std::vector<int32_t> &cnt) {
+    std::vector<uint8_t> keep((size_t)B * N);
+    rattn_status st = read_back(keep.data(), keep_dev, keep.size(), s);
+    if (st != RATTN_OK) return st;
+    cnt.assign((size_t)B, 0);
+    for (int b = 0; b < B; ++b) {
+        const uint8_t *row = keep.data() + (size_t)b * N;
+        int c = 0;
+        for (int n = 0; n < N; ++n) c += row[n] != 0;
+        cnt[b] = c;
+    }
+    return RATTN_OK;
+}
+
+// The bound passed with a padded batch must cover every image's kept count.
+rattn_status validate_bound(const uint8_t *keep_dev, int B, int N, int bound, hipStream_t s) {
+    std::vector<int32_t> cnt;
+    rattn_status st = kept_counts(keep_dev, B, N, s, cnt);
+    if (st != RATTN_OK) return st;
+    for (int b = 0; b < B; ++b)
+        if (cnt[b] > bound) return RATTN_ERR_INVALID_ARG;
+    return RATTN_OK;
+}
+
+// cu_seqlens must be the prefix sum of the mask's kept counts.
+rattn_status validate_cu_against_mask(const int32_t *cu_dev, const uint8_t *keep_dev, int B,
+                                      int N, hipStream_t s) {
+    std::vector<int32_t> cu, cnt;
+    int longest = 0;
+    rattn_status st = validate_cu(cu_dev, B, s, cu, &longest);
+    if (st != RATTN_OK) return st;
+    st = kept_counts(keep_dev, B, N, s, cnt);
+    if (st != RATTN_OK) return st;
+    for (int b = 0; b < B; ++b)
+        if ((int64_t)cu[b + 1] - cu[b] != cnt[b]) return RATTN_ERR_INVALID_ARG;
+    return RATTN_OK;
 }
 
 }  // namespace
@@ -75,7 +152,11 @@ const char *rattn_status_string(rattn_status s) {
     return "RATTN_ERR_UNKNOWN";
 }
 
-int rattn_version(void) { return (1 << 16) | 0; }
+int rattn_version(void) { return (1 << 16) | 1; }
+
+int rattn_set_validate(int on) { return g_validate.exchange(on != 0 ? 1 : 0); }
+
+int rattn_get_validate(void) { return g_validate.load(); }
 
 rattn_status rattn_pack(const void *const *src, void *const *dst, int n_tensors,
                         const uint8_t *keep, int B, int N, int row_elems, rattn_dtype dt,
@@ -128,6 +209,13 @@ rattn_status rattn_forward(const void *q, const void *k, const void *v, void *o,
         return RATTN_ERR_INVALID_ARG;
     rattn_status st = rattn_init();
     if (st != RATTN_OK) return st;
+    if (validating()) {
+        std::vector<int32_t> cu;
+        int longest = 0;
+        st = validate_cu(cu_seqlens, B, (hipStream_t)stream, cu, &longest);
+        if (st != RATTN_OK) return st;
+        if (longest > max_seqlen) return RATTN_ERR_INVALID_ARG;
+    }
     AttnArgs a;
     a.q = q;
     a.k = k;
@@ -155,6 +243,10 @@ rattn_status rattn_unpack(const void *src, void *dst_padded, void *cls, const ui
     if ((dst_padded && !aligned16(dst_padded)) || (cls && !aligned16(cls))) return RATTN_ERR_INVALID_ARG;
     rattn_status st = rattn_init();
     if (st != RATTN_OK) return st;
+    if (validating()) {
+        st = validate_cu_against_mask(cu_seqlens, keep, B, N, (hipStream_t)stream);
+        if (st != RATTN_OK) return st;
+    }
     UnpackArgs a;
     a.src = (const u32x4 *)src;
     a.dst = (u32x4 *)dst_padded;
@@ -187,6 +279,12 @@ rattn_status rattn_repack(const void *const *src, void *const *dst, int n_tensor
     }
     rattn_status st = rattn_init();
     if (st != RATTN_OK) return st;
+    if (validating()) {
+        std::vector<int32_t> cu;
+        int longest = 0;
+        st = validate_cu(cu_seqlens, B, (hipStream_t)stream, cu, &longest);
+        if (st != RATTN_OK) return st;
+    }
     RepackArgs a;
     for (int i = 0; i < kMaxTensors; ++i) {
         a.src[i] = i < n_tensors ? (const u32x4 *)src[i] : nullptr;
@@ -226,6 +324,11 @@ rattn_status fused_common(const void *q, const void *k, const void *v, const uin
         return RATTN_ERR_INVALID_ARG;
     rattn_status st = rattn_init();
     if (st != RATTN_OK) return st;
+    if (validating()) {
+        // the bound (pad_len for the padded comparator) must cover every image
+        st = validate_bound(keep, B, N, max_seqlen, (hipStream_t)stream);
+        if (st != RATTN_OK) return st;
+    }
     FusedArgs a;
     a.q = q;
     a.k = k;

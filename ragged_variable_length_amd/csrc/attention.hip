@@ -338,7 +338,10 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
     const int vr = 4 * grp + (col >> 2);
     const int vp = (col & 3) >> 1, vhalf = 4 * (col & 1);
     constexpr float kLag = 8.f;
-    const float lag = kPos ? kLag / c : 0.f;
+    // in raw units; finite even when c is so small that 8 / c overflows
+    // (scale below about 1.6e-38), so that m + lag stays -inf on the first
+    // chunk and the first chunk always sets the reference
+    const float lag = kPos ? fminf(kLag / c, 3.4028234663852886e38f) : 0.f;
     float m[QB], mc[QB];
     f32x4 acc[QB][4], accl[QB];
     auto reset = [&]() {
@@ -438,17 +441,25 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
                 // was used.  One test covers all blocks, on each lane's own
                 // maximum: some lane's exceeds m + lag exactly when the
                 // maximum over the four lanes of that query does, so the
-                // cross-lane reduction runs only when rescaling.
+                // cross-lane reduction runs only when rescaling.  Inside the
+                // branch each query row decides for itself: only a row whose
+                // own maximum passed its lag moves its reference (to that
+                // maximum, exactly); every other row keeps its reference and
+                // multiplies by exactly 1.  So a row's probabilities, and
+                // their rounding, depend on that row's scores alone, not on
+                // the other rows of the wavefront, the tile shape or the
+                // sequence bound.
                 bool grow = false;
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb) grow = grow || mx[qb] > m[qb] + lag;
                 if (__ballot(grow)) {
 #pragma unroll
                     for (int qb = 0; qb < QB; ++qb) {
-                        const float mn = vmax(m[qb], max_across_groups(mx[qb]));
-                        const float alpha = fast_exp2((m[qb] - mn) * c);
-                        m[qb] = mn;
-                        mc[qb] = mn * c;
+                        const float mxa = max_across_groups(mx[qb]);
+                        const bool row_grows = mxa > m[qb] + lag;
+                        const float alpha = row_grows ? fast_exp2((m[qb] - mxa) * c) : 1.f;
+                        m[qb] = row_grows ? mxa : m[qb];
+                        mc[qb] = m[qb] * c;
 #pragma unroll
                         for (int dt = 0; dt < 4; ++dt) acc[qb][dt] *= alpha;
                         accl[qb][0] *= alpha;

@@ -69,6 +69,20 @@ static PyObject *py_version(PyObject *self, PyObject *const *args, Py_ssize_t na
     return PyLong_FromLong(rattn_version());
 }
 
+static PyObject *py_set_validate(PyObject *self, PyObject *const *args, Py_ssize_t nargs) {
+    (void)self;
+    if (nargs_is(nargs, 1, "set_validate")) return NULL;
+    INT(0, on);
+    return PyLong_FromLong(rattn_set_validate(on));
+}
+
+static PyObject *py_get_validate(PyObject *self, PyObject *const *args, Py_ssize_t nargs) {
+    (void)self;
+    (void)args;
+    if (nargs_is(nargs, 0, "get_validate")) return NULL;
+    return PyLong_FromLong(rattn_get_validate());
+}
+
 /* pack(srcs: sequence of int, dsts: sequence of int, keep, B, N, row_elems,
  *      dtype, cu_seqlens, max_seqlen_out|None, total_out|None, stream) */
 static PyObject *py_pack(PyObject *self, PyObject *const *args, Py_ssize_t nargs) {
@@ -248,6 +262,10 @@ static PyMethodDef methods[] = {
     {"status_string", (PyCFunction)(void (*)(void))py_status_string, METH_FASTCALL,
      "rattn_status_string(status)"},
     {"version", (PyCFunction)(void (*)(void))py_version, METH_FASTCALL, "rattn_version()"},
+    {"set_validate", (PyCFunction)(void (*)(void))py_set_validate, METH_FASTCALL,
+     "rattn_set_validate(on)"},
+    {"get_validate", (PyCFunction)(void (*)(void))py_get_validate, METH_FASTCALL,
+     "rattn_get_validate()"},
     {"pack", (PyCFunction)(void (*)(void))py_pack, METH_FASTCALL, "rattn_pack(...)"},
     {"forward", (PyCFunction)(void (*)(void))py_forward, METH_FASTCALL, "rattn_forward(...)"},
     {"unpack", (PyCFunction)(void (*)(void))py_unpack, METH_FASTCALL, "rattn_unpack(...)"},

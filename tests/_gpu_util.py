@@ -9,7 +9,12 @@ import torch
 import oracle
 from ragged_variable_length_amd import RaggedPipeline
 
-# Attention tolerances, max |gpu - oracle| over kept rows (unit-normal inputs).
+# Attention tolerances, max |gpu - oracle| over kept rows (unit-normal inputs
+# at the ViT scale 1/sqrt(64), where outputs stay well inside (-2, 2)).  The
+# edge cases at scale 0.5, four times that, are held to the derived bound
+# below only: the softmax then concentrates on a few keys, |o| reaches 3-4,
+# and half a bf16 ulp there (0.0078) plus the rounding of P passes 1e-2
+# (measured 0.0128 on MI355X at N = 300, a quarter of the derived bound).
 FLAT_TOL = {"f32": 1e-4, "f16": 2e-3, "bf16": 1e-2}
 # Unit round-off of the 16-bit types: the kernel rounds the probabilities and
 # the output once each, so the rounding error of an element is at most
@@ -101,3 +106,104 @@ def sample_rows(cu: np.ndarray, n: int, seed: int = 0) -> np.ndarray:
     lasts = cu[1:][np.diff(cu) > 0] - 1
     extra = rng.choice(T, size=min(n, T), replace=False) if T else np.zeros(0, np.int64)
     return np.unique(np.concatenate([firsts, lasts, extra]).astype(np.int64))
+
+
+def whole_images(cu: np.ndarray, n_extra: int = 4, min_long: int = 0, n_long: int = 0,
+                 seed: int = 0) -> np.ndarray:
+    """Images to check whole: the longest, the shortest non-empty one, n_long
+    images longer than min_long and n_extra more, all seeded; sorted, unique."""
+    rng = np.random.default_rng(seed)
+    L = np.diff(cu)
+    nz = np.nonzero(L > 0)[0]
+    picks = [int(np.argmax(L)), int(nz[np.argmin(L[nz])])]
+    longs = np.nonzero(L > min_long)[0]
+    if n_long and longs.size:
+        picks += rng.choice(longs, size=min(n_long, longs.size), replace=False).tolist()
+    picks += rng.choice(nz, size=min(n_extra, nz.size), replace=False).tolist()
+    return np.unique(np.asarray(picks, dtype=np.int64))
+
+
+def rows_of_images(cu: np.ndarray, images) -> np.ndarray:
+    """Every flat row of the listed images."""
+    parts = [np.arange(cu[b], cu[b + 1], dtype=np.int64) for b in images]
+    return np.concatenate(parts) if parts else np.zeros(0, np.int64)
+
+
+def flat_rows_of_positions(keep, positions) -> np.ndarray:
+    """Flat (packed) rows of the kept ones among padded positions b * N + n."""
+    k = (np.asarray(keep) != 0).reshape(-1)
+    rank = np.cumsum(k) - 1
+    pos = np.asarray(positions, dtype=np.int64).reshape(-1)
+    pos = pos[k[pos]]
+    return np.unique(rank[pos].astype(np.int64))
+
+
+def check_rows(w, cu, nrows: int, n_whole_extra: int, min_long: int = 0,
+               n_long: int = 0) -> np.ndarray:
+    """Rows checked at the full-size workloads: first and last row of every
+    image and a seeded sample, every row of the longest, the shortest and
+    several more images (n_long of them longer than min_long), and every kept
+    outlier row."""
+    rows = [sample_rows(cu, nrows, seed=w.seed),
+            rows_of_images(cu, whole_images(cu, n_whole_extra, min_long, n_long, seed=w.seed))]
+    if w.outlier_positions is not None:
+        rows.append(flat_rows_of_positions(w.keep.numpy(), w.outlier_positions.numpy()))
+    return np.unique(np.concatenate(rows))
+
+
+def keep_length_range(B, N, lo, hi, seed):
+    """Keep mask whose image b keeps a random subset of lo..hi positions."""
+    g = torch.Generator().manual_seed(seed)
+    keep = torch.zeros((B, N), dtype=torch.uint8)
+    for b in range(B):
+        L = int(torch.randint(lo, hi + 1, (1,), generator=g))
+        keep[b, torch.randperm(N, generator=g)[:L]] = 1
+    return keep
+
+
+def late_outlier_keys(seed=71, B=32, N=300, H=8, lo=130, hi=250, frac=0.04, name=None):
+    """bf16 N(0,1) q/k/v whose images keep lo..hi of N positions, with a few
+    key rows at kept ranks 64 and beyond scaled by 8 (exact in bf16): their
+    scores pass the first 64-key chunk's maximum by far more than the lazy
+    softmax reference may lag, so those query rows move their reference after
+    the first chunk while the other rows of their wavefront do not.  N = 300
+    selects 128-row tiles for the bound N and 64-row tiles for the exact bound
+    (at most 250)."""
+    import workloads
+    keep = keep_length_range(B, N, lo, hi, seed)
+    w = workloads.custom(B, N, H, "bf16", keep=keep, seed=seed + 1,
+                         name=name or f"late_outlier_keys_{N}")
+    g = torch.Generator().manual_seed(seed + 2)
+    k = w.k.float()
+    for b in range(B):
+        late = torch.nonzero(keep[b]).flatten()[64:]
+        n = max(1, int(frac * late.numel()))
+        k[b, late[torch.randperm(late.numel(), generator=g)[:n]]] *= 8.0
+    w.k = k.to(torch.bfloat16).contiguous()
+    return w
+
+
+def check_padded(w, out, cls, o64, absw, rows=None, flat=True):
+    """A padded output and its CLS rows against the oracle: pruned rows are
+    all-zero bytes, CLS rows are bitwise the output rows (b, 0), and the kept
+    rows, gathered in (b, n) order (all, or the listed flat rows), are within
+    the flat tolerance (with `flat`) and the derived rounding bound."""
+    keep = w.keep.numpy() != 0
+    ob = bits(out)
+    assert not ob[~keep].any(), "pruned output rows are not all-zero bytes"
+    if cls is not None:
+        cb = bits(cls)
+        for b in range(w.B):
+            assert np.array_equal(cb[b], ob[b, 0]), f"CLS row of image {b} differs from out[b, 0]"
+    got = oracle.widen(oracle.pack(out, w.keep), w.dtype).reshape(-1, w.H, w.D)
+    if rows is not None:
+        got = got[rows]
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - o64)
+    bound = FLAT_TOL[w.dtype] + 2.0 * UNIT_ROUNDOFF[w.dtype] * (np.abs(o64) + absw)
+    e = float(err.max()) if err.size else 0.0
+    r = float((err / bound).max()) if err.size else 0.0
+    say(f"{w.name}: max|err|={e:.3e} err/bound={r:.3f}")
+    if flat:
+        assert e <= FLAT_TOL[w.dtype], e
+    assert r <= 1.0, r

@@ -151,6 +151,14 @@ inline hipError_t hipGetLastError() { return hipSuccess; }
 
 // --- host API subset used by api.hip (emulation: one fake gfx950 device) ---
 struct hipDeviceProp_t { char gcnArchName[256]; };
+// device memory is host memory here, and launches run to completion when
+// they are made, so a device-to-host copy is a memcpy and a stream is always idle
+enum hipMemcpyKind { hipMemcpyHostToDevice = 1, hipMemcpyDeviceToHost = 2, hipMemcpyDeviceToDevice = 3 };
+inline hipError_t hipMemcpyAsync(void *dst, const void *src, size_t n, hipMemcpyKind, hipStream_t) {
+    memcpy(dst, src, n);
+    return hipSuccess;
+}
+inline hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
 inline hipError_t hipGetDeviceCount(int *n) { *n = 1; return hipSuccess; }
 inline hipError_t hipGetDevice(int *d) { *d = 0; return hipSuccess; }
 inline hipError_t hipGetDeviceProperties(hipDeviceProp_t *p, int) { strcpy(p->gcnArchName, "gfx950:sramecc+:xnack-"); return hipSuccess; }

@@ -115,3 +115,96 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, cwd=ROOT, timeout=300)
     assert p.returncode == 2
     assert "one GPU" in p.stderr
+
+
+# ---------------------------------------------------------------------------
+# the other byte counts and the flop count, tallied item by item; the pages'
+# FLOP figure at 80 % pruning
+# ---------------------------------------------------------------------------
+def _count_three_call_bytes(keep, H, es):
+    """rattn_pack: the mask, and every kept q, k, v row read and written;
+    rattn_forward: every kept q, k, v row read and o row written; rattn_unpack:
+    the mask, every kept o row read, every padded output row and one CLS row
+    per image written."""
+    row = H * 64 * es
+    total = 0
+    for image in keep:
+        total += len(image)                   # pack reads the mask
+        total += len(image)                   # unpack reads it again
+        for flag in image:
+            if flag:
+                total += 3 * 2 * row          # pack: q, k, v read and written
+                total += 4 * row              # forward: q, k, v read, o written
+                total += row                  # unpack: o row read
+            total += row                      # unpack: padded row written
+        total += row                          # unpack: CLS row written
+    return total
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_three_call_bytes_matches_a_tally_over_the_mask(dtype):
+    keep = [[1, 0, 1, 1], [0, 0, 0, 0], [1, 1, 0, 1]]
+    T = sum(map(sum, keep))
+    got = bench.three_call_bytes(T, len(keep), len(keep[0]), 3, dtype)
+    assert got == _count_three_call_bytes(keep, 3, bench.ES[dtype])
+
+
+def _count_repack_bytes(keep2_per_image, H, es):
+    """rattn_repack of q, k and v: the second flag of every flat row read,
+    every row kept again read and written in each tensor, the input
+    cu_seqlens read and the output cu_seqlens written (int32, B + 1 each)."""
+    row = H * 64 * es
+    total = 0
+    for flags in keep2_per_image:
+        for f in flags:
+            total += 1
+            if f:
+                total += 3 * 2 * row
+    B = len(keep2_per_image)
+    total += 4 * (B + 1) + 4 * (B + 1)
+    return total
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_repack_bytes_matches_a_tally(dtype):
+    flags = [[1, 0, 1], [0], [], [1, 1, 1, 0, 1]]
+    T = sum(len(f) for f in flags)
+    T2 = sum(map(sum, flags))
+    got = bench.repack_bytes(T, T2, len(flags), 2, dtype)
+    assert got == _count_repack_bytes(flags, 2, bench.ES[dtype])
+
+
+def test_attention_flops_matches_a_tally_over_pairs():
+    # per head, every (query, key) pair of the same image costs one 64-term dot
+    # product (64 multiplies, 64 adds) and one 64-wide p * v accumulation
+    # (64 multiplies, 64 adds)
+    lengths, H = [3, 0, 1, 5], 2
+    tally = 0
+    for L in lengths:
+        for _h in range(H):
+            for _i in range(L):
+                for _j in range(L):
+                    tally += 2 * 64 + 2 * 64
+    assert bench.attention_flops(lengths, H) == tally
+
+
+def test_attention_flops_reproduce_the_pages_reduction_at_80pct_pruning():
+    """The write-up's lead paragraph: 80 % token pruning cuts attention FLOPs
+    by 96 %; its section on FlashAttention-2's dispatch ceiling: DeiT-Base goes
+    from 197 to about 39 tokens per image.  The count here gives that figure
+    for the pages' token counts and for the serving sweep's nominal 80 % count
+    (round(0.2 * 196) patches plus CLS)."""
+    import json
+    import workloads
+    with open(os.path.join(ROOT, "tests", "golden", "pages_numbers.json")) as f:
+        items = json.load(f)["items"]
+    tokens = next(i for i in items if "tokens_after_about" in i)
+    flops = next(i for i in items if "attention_flop_reduction" in i)
+    assert tokens["prune_rate"] == flops["prune_rate"] == 0.8
+    B, H = 32, 12  # the write-up's DeiT-Base batch of 32
+    full = bench.attention_flops([tokens["tokens_before"]] * B, H)
+    for after in (tokens["tokens_after_about"], workloads.sweep_kept_count(0.8)):
+        reduction = 1.0 - bench.attention_flops([after] * B, H) / full
+        assert round(reduction, 2) == flops["attention_flop_reduction"], (after, reduction)
+    # and the closed form (1 - p)^2 of the kept fraction
+    assert round(1.0 - (1.0 - flops["prune_rate"]) ** 2, 2) == flops["attention_flop_reduction"]

@@ -211,3 +211,22 @@ def test_repack_argument_checks(lib):
     assert f(src, dst, 1, A, A, 2, 128, BF16, A, None, None) == INVALID       # cu_out aliases cu
     assert f(src, P2(A), 1, A, A, 2, 128, BF16, A + 64, None, None) == INVALID  # dst == src
     assert f(src, dst, 1, A, A, 2, 5, F32, A + 64, None, None) == INVALID     # row not 16 B
+
+
+def test_validate_mode_switch(lib):
+    """The debug-validate switch is a process-wide flag: set returns the
+    previous setting; no device is needed to flip it."""
+    prev = lib.rattn_get_validate()
+    try:
+        assert lib.rattn_set_validate(1) == prev
+        assert lib.rattn_get_validate() == 1
+        assert lib.rattn_set_validate(7) == 1      # any nonzero value means on
+        assert rv.rattn_get_validate() is True
+        assert rv.rattn_set_validate(False) is True
+        assert lib.rattn_get_validate() == 0
+        # host-side checks still come first in the mode: nothing is read back
+        lib.rattn_set_validate(1)
+        assert _fwd(lib, D=32) == UNSUPPORTED
+        assert _fwd(lib, q=None) == INVALID
+    finally:
+        lib.rattn_set_validate(prev)

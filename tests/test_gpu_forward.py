@@ -24,7 +24,8 @@ import torch
 
 import oracle
 import workloads
-from tests._gpu_util import FLAT_TOL, UNIT_ROUNDOFF, bits, sample_rows, say
+from tests._gpu_util import (FLAT_TOL, UNIT_ROUNDOFF, bits, check_rows, late_outlier_keys,
+                             say)
 
 pytestmark = pytest.mark.gpu
 CANARY = 0x5A
@@ -122,13 +123,13 @@ def test_forward_deit_b_sweep_bf16(B, p, exact):
     full(workloads.deit_b_sweep(B, p, exact_unpruned=exact))
 
 
-def _sampled(w, nrows, flat):
-    say(f"{w.name}: B={w.B} N={w.N} H={w.H} {w.dtype} T={w.total_kept} (sampled rows)")
+def _sampled(w, nrows, flat, **pick):
     o, T = run_forward(w)
     cu, _, T2 = oracle.scan(w.keep)
     assert T2 == T
     pq, pk, pv = (oracle.pack(t, w.keep) for t in (w.q, w.k, w.v))
-    rows = sample_rows(cu, nrows, seed=w.seed)
+    rows = check_rows(w, cu, nrows, **pick)
+    say(f"{w.name}: B={w.B} N={w.N} H={w.H} {w.dtype} T={T}: {len(rows)} rows checked")
     o64, absw = oracle.attention(*(oracle.widen(t, w.dtype).reshape(T, w.H, w.D)
                                    for t in (pq, pk, pv)), cu, w.scale, rows=rows,
                                  want_absw=True)
@@ -137,14 +138,16 @@ def _sampled(w, nrows, flat):
 
 
 def test_forward_deit_b_384_50pct_outliers_bf16():
+    # whole images (the longest, the shortest, four longer than 256 and two
+    # more) and every kept outlier row, besides the sample
     w = workloads.deit_b_384()
-    o, T = _sampled(w, nrows=160, flat=False)
+    o, T = _sampled(w, nrows=160, flat=False, n_whole_extra=2, min_long=256, n_long=4)
     assert np.array_equal(bits(o[:T]), fused_kept_rows(w)), "forward != fused"
 
 
 def test_forward_large_batch_threshold_bf16():
     w = workloads.large_batch()
-    o, T = _sampled(w, nrows=400, flat=True)
+    o, T = _sampled(w, nrows=400, flat=True, n_whole_extra=6)
     assert np.array_equal(bits(o[:T]), fused_kept_rows(w)), "forward != fused"
 
 
@@ -164,7 +167,7 @@ def test_forward_ragged_tails(dtype):
     lengths = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200]
     keep = _keep_with_lengths(lengths, 200, seed=3)
     w = workloads.custom(len(lengths), 200, 2, dtype, keep=keep, seed=11, name=f"fwd_tails_{dtype}")
-    o, T = full(w, flat=False)
+    o, T = full(w, flat=True)
     assert np.array_equal(bits(o[:T]), fused_kept_rows(w)), "forward != fused"
 
 
@@ -174,7 +177,7 @@ def test_forward_length_one_returns_v_row(dtype):
     keep = torch.zeros((B, N), dtype=torch.uint8)
     keep[:, 0] = 1
     w = workloads.custom(B, N, 3, dtype, keep=keep, seed=12, name=f"fwd_len1_{dtype}")
-    o, T = full(w, flat=False)
+    o, T = full(w, flat=True)
     assert np.array_equal(bits(o[:T]), bits(w.v[:, 0]))
 
 
@@ -183,7 +186,7 @@ def test_forward_empty_images():
     keep = torch.zeros((B, N), dtype=torch.uint8)
     keep[1, [3, 9, 10]] = 1
     keep[3, :] = 1
-    full(workloads.custom(B, N, 2, "bf16", keep=keep, seed=13, name="fwd_empty"), flat=False)
+    full(workloads.custom(B, N, 2, "bf16", keep=keep, seed=13, name="fwd_empty"), flat=True)
 
 
 def test_forward_nothing_to_do_writes_nothing():
@@ -200,7 +203,7 @@ def test_forward_long_sequences(N):
     keep = torch.ones((2, N), dtype=torch.uint8)
     keep[1, N // 3:] = 0
     w = workloads.custom(2, N, 2, "bf16", keep=keep, seed=15, name=f"fwd_long_{N}")
-    o, T = full(w, flat=False)
+    o, T = full(w, flat=True)
     assert np.array_equal(bits(o[:T]), fused_kept_rows(w)), "forward != fused"
 
 
@@ -295,7 +298,7 @@ def test_forward_cross_image_isolation():
 @pytest.mark.parametrize("scale", [0.0, -0.125, 0.5])
 def test_forward_unusual_scales(scale):
     full(workloads.custom(4, 90, 2, "bf16", p_keep=0.7, seed=17, scale=scale,
-                          name=f"fwd_scale_{scale}"), flat=False)
+                          name=f"fwd_scale_{scale}"), flat=scale != 0.5)
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.125, 0.5])
@@ -304,7 +307,7 @@ def test_forward_unusual_scales_two_block_tiles(scale):
     # 32 x 8 = 256 heads give one workgroup per head, so each copies the next
     # tile's Q rows while its current tile finishes
     full(workloads.custom(32, 300, 8, "bf16", p_keep=0.9, seed=19, scale=scale,
-                          name=f"fwd_scale_{scale}_128_row_tiles"), flat=False)
+                          name=f"fwd_scale_{scale}_128_row_tiles"), flat=scale != 0.5)
 
 
 def test_forward_side_stream():
@@ -315,3 +318,28 @@ def test_forward_side_stream():
     with torch.cuda.stream(s):
         o, T = run_forward(w, stream=s)
     check(w, o, T, ref["o64"], ref["absw"])
+
+
+def test_forward_late_rescale_is_per_row_across_bounds():
+    """Rows whose softmax reference moves after the first chunk next to rows
+    whose reference does not: the bound N (128-row tiles) and the exact bound
+    (64-row tiles) give the same bits, within the oracle's rounding bound, and
+    the fused kernel's bits."""
+    w = late_outlier_keys(name="fwd_late_outlier_keys")
+    flat_cu = host_flat(w)
+    say(f"{w.name}: late outlier keys, bound N vs exact")
+    ref = oracle.pipeline(w, want_absw=True)
+    a, T = run_forward(w, max_seqlen=w.N, flat_cu=flat_cu)
+    check(w, a, T, ref["o64"], ref["absw"], flat=False)
+    b, _ = run_forward(w, max_seqlen=max(w.kept_counts), flat_cu=flat_cu)
+    assert np.array_equal(bits(a), bits(b))
+    assert np.array_equal(bits(a[:T]), fused_kept_rows(w)), "forward != fused"
+
+
+@pytest.mark.parametrize("N", [90, 300])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_forward_tiny_positive_scale(dtype, N):
+    """scale 1e-39: 8 / (scale log2 e) overflows float32; the output is the
+    mean of the image's V rows."""
+    full(workloads.custom(4, N, 2, dtype, p_keep=0.7, seed=23, scale=1e-39,
+                          name=f"fwd_scale_1e-39_{dtype}_{N}"), flat=True)

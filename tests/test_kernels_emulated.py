@@ -12,8 +12,8 @@ rattn_fused_padded bitwise against rattn_fused, and rattn_repack bit-exact
 against the oracle.  Any out-of-bounds global or
 LDS access aborts the run.
 
-These cases cover the three-call path, whose GPU parity tests are kept off the
-GPU (see test_gpu_parity.py).  The emulation does not model timing, memory
+These cases run the same kernels as the GPU parity tests, on the host, where
+AddressSanitizer can see every access.  The emulation does not model timing, memory
 ordering between workgroups or the wave scheduler, so it cannot show a hang or
 a race; it shows indexing, bounds and arithmetic.
 """

@@ -57,6 +57,8 @@ class Workload:
     scale: float = SCALE
     seed: int = 0
     meta: dict = field(default_factory=dict)
+    # padded row indices b * N + n scaled as outliers (384 px workload), else None
+    outlier_positions: torch.Tensor | None = None
 
     @property
     def row_elems(self) -> int:
@@ -218,7 +220,8 @@ def deit_b_384(seed: int | None = None, B: int = 64) -> Workload:
         x[rows] *= 8.0
         qkv.append(_cast(x.view(B, N, H, HEAD_DIM), "bf16"))
     return Workload("deit_b_384_50pct", B, N, H, HEAD_DIM, "bf16", keep, *qkv, seed=seed,
-                    meta={"prune": 0.5, "outlier_rows": n_out, "std": 0.5})
+                    meta={"prune": 0.5, "outlier_rows": n_out, "std": 0.5},
+                    outlier_positions=rows.sort().values)
 
 
 def large_batch(seed: int | None = None, B: int = 512) -> Workload:
