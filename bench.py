@@ -38,7 +38,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 import workloads  # noqa: E402
-from ragged_variable_length_amd import FusedPlan, RaggedPipeline, rattn_init  # noqa: E402
+from ragged_variable_length_amd import (FusedPlan, RaggedPipeline, rattn_forward,  # noqa: E402
+                                        rattn_fused, rattn_init)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, datasheet
 # HBM traffic of the fused kernel measured with rocprofv3 counters (FETCH_SIZE,
@@ -245,10 +246,12 @@ def timing_lib():
         lib.bench_call_floor.argtypes = [step, i32, i32, i32, stats]
         lib.bench_enqueue_cost.argtypes = [step, i32, i32, stats]
         lib.bench_graph_floor.argtypes = [step, i32, i32, i32, stats]
+        lib.bench_graph_enqueue_cost.argtypes = [step, i32, i32, stats]
         lib.bench_loop.argtypes = [step, i32, i32]
         lib.bench_peaks.argtypes = [i32, i32, P, ctypes.POINTER(BenchPeaks)]
         for f in (lib.bench_empty_floor, lib.bench_call_floor, lib.bench_enqueue_cost,
-                  lib.bench_graph_floor, lib.bench_loop, lib.bench_peaks):
+                  lib.bench_graph_floor, lib.bench_graph_enqueue_cost, lib.bench_loop,
+                  lib.bench_peaks):
             f.restype = i32
         _timing = lib
     return _timing
@@ -417,6 +420,45 @@ def three_call_and_stacks(r: Resident, reps: int) -> dict:
     }
 
 
+def python_call_floor(call, stream, iters: int, warmup: int) -> dict:
+    """Host call -> completion through Python: `call()` then a stream
+    synchronisation, timed with time.perf_counter_ns around both."""
+    ts = []
+    for i in range(warmup + iters):
+        t0 = time.perf_counter_ns()
+        call()
+        stream.synchronize()
+        t1 = time.perf_counter_ns()
+        if i >= warmup:
+            ts.append((t1 - t0) / 1000.0)
+    ts.sort()
+    n = len(ts)
+    at = lambda f: ts[min(n - 1, int(f * (n - 1) + 0.5))]
+    return {"median_us": round(at(0.5), 2), "p5_us": round(at(0.05), 2),
+            "p95_us": round(at(0.95), 2), "mean_us": round(sum(ts) / n, 2),
+            "min_us": round(ts[0], 2)}
+
+
+def python_floors(r: Resident, stream, iters: int, warmup: int) -> dict:
+    """The product's own Python path, call -> completion: FusedPlan.run()
+    (checked and marshalled once), rattn_fused() with its per-call checks and
+    marshalling, and rattn_forward() on flat buffers; next to a one-element
+    torch in-place add on the same stream, the framework's own floor."""
+    w = r.w
+    f = FlatResident(w, stream)
+    one = torch.zeros(1, device="cuda")
+    calls = {
+        "fused_plan_run": r.plan.run,
+        "fused_call": lambda: rattn_fused(r.q, r.k, r.v, r.keep, w.scale, out_padded=r.out,
+                                          cls=r.cls, stream=stream),
+        "forward_call": lambda: rattn_forward(f.flat[0], f.flat[1], f.flat[2], f.o, f.cu, w.N,
+                                              w.scale, stream=stream),
+        "torch_add_one_element": lambda: one.add_(1.0),
+    }
+    with torch.cuda.stream(stream):
+        return {name: python_call_floor(c, stream, iters, warmup) for name, c in calls.items()}
+
+
 def dispatch_floors(stream, iters: int, warmup: int) -> dict:
     """Host call -> completion (C++ steady_clock) at serving batch sizes 1-4,
     80 % pruning, DeiT-B shape: the one-launch rattn_fused (also enqueue-only
@@ -441,6 +483,8 @@ def dispatch_floors(stream, iters: int, warmup: int) -> dict:
         row["fused_enqueue_us"] = st.as_dict()
         if lib.bench_graph_floor(ctypes.byref(cs), WHAT_FUSED, iters, warmup, ctypes.byref(st)) == 0:
             row["fused_graph_replay_sync_us"] = st.as_dict()
+        if lib.bench_graph_enqueue_cost(ctypes.byref(cs), WHAT_FUSED, iters, ctypes.byref(st)) == 0:
+            row["fused_graph_launch_enqueue_us"] = st.as_dict()
         sr = StackResident(r)  # owns the flat buffers tc points into
         tc = sr.c_step()
         if lib.bench_call_floor(ctypes.byref(tc), WHAT_THREE_CALL, iters, warmup, ctypes.byref(st)):
@@ -454,11 +498,17 @@ def dispatch_floors(stream, iters: int, warmup: int) -> dict:
                                 ctypes.byref(st)):
             raise RuntimeError("bench_call_floor (forward) failed")
         row["forward_call_sync_us"] = st.as_dict()
+        row["python_call_sync_us"] = python_floors(r, stream, iters, warmup)
         res[f"deit_b_B{B}_p80"] = row
         print(f"[bench] dispatch floor B={B}: fused call+sync {row['fused_call_sync_us']['median_us']} us,"
               f" enqueue {row['fused_enqueue_us']['median_us']} us, rattn_forward alone call+sync "
               f"{row['forward_call_sync_us']['median_us']} us, three calls + sync "
               f"{row['three_call_call_sync_us']['median_us']} us", flush=True)
+        py = row["python_call_sync_us"]
+        print(f"[bench] Python path B={B}: FusedPlan.run+sync {py['fused_plan_run']['median_us']} us,"
+              f" rattn_fused()+sync {py['fused_call']['median_us']} us, rattn_forward()+sync "
+              f"{py['forward_call']['median_us']} us, torch one-element add+sync "
+              f"{py['torch_add_one_element']['median_us']} us", flush=True)
     # every point of the serving sweep: the one launch, host call + sync and
     # device time back to back
     sweep = {}
@@ -702,30 +752,41 @@ def tiny_fp32(stream, launches: int) -> dict:
     return out
 
 
-def cpu_baseline(w, budget_s: float) -> dict:
-    """The CPU oracle (plain C, fp64, one thread) on the same workload: whole
-    batches of scan, pack, attention and unpack until the budget is used."""
-    import oracle  # test infrastructure; used only for this reported baseline
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        res = oracle.pipeline(w)
-        oracle.unpack(res["o64"], w.keep, res["cu"])
-        reps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(reps * w.B / dt, 2), "unit": "seqs/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} full batch(es) of the {w.name} workload (B={w.B}) through the fp64 "
-                      f"oracle's scan, pack, attention and unpack, {dt:.1f} s on 1 host thread"}
+def cpu_model() -> dict:
+    """The host CPU: model name (from /proc/cpuinfo), logical CPUs, and the
+    CPUs this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count() or 1
+    return {"model": model, "logical_cpus": os.cpu_count() or 1, "usable_cpus": usable}
 
 
-def _oracle_batches(maker: str, budget_s: float) -> tuple:
-    """Worker of cpu_baseline_all_cores: the one-thread loop of cpu_baseline
-    on a workload rebuilt from its seed (workloads.by_name(maker)); returns
-    (batches, seconds)."""
+def _sub_workload(w, n_images: int):
+    """The first n_images images of a workload (a bounded sample of it)."""
+    if n_images >= w.B:
+        return w
+    import copy
+    s = copy.copy(w)
+    s.B = n_images
+    s.keep = w.keep[:n_images].contiguous()
+    s.q, s.k, s.v = (t[:n_images].contiguous() for t in (w.q, w.k, w.v))
+    return s
+
+
+def _oracle_loop(w, budget_s: float) -> tuple:
+    """Whole batches of the fp64 oracle's scan, pack, attention and unpack on
+    w until the budget is used; returns (batches, seconds)."""
     import oracle  # test infrastructure; used only for this reported baseline
-    w = workloads.by_name(maker)
     t0 = time.perf_counter()
     reps = 0
     while True:
@@ -737,24 +798,67 @@ def _oracle_batches(maker: str, budget_s: float) -> tuple:
     return reps, time.perf_counter() - t0
 
 
+def cpu_baseline(w, budget_s: float, sample_images: int | None = None) -> dict:
+    """The CPU oracle (plain C, fp64, one thread) on the same workload, or on
+    its first `sample_images` images: whole batches until the budget is used,
+    images per second."""
+    s = _sub_workload(w, sample_images) if sample_images else w
+    reps, dt = _oracle_loop(s, budget_s)
+    what = (f"the first {s.B} of the {w.B} images" if s.B < w.B else f"all {w.B} images")
+    return {"value": round(reps * s.B / dt, 2), "unit": "seqs/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} pass(es) over {what} of the {w.name} workload through the fp64 "
+                      f"oracle's scan, pack, attention and unpack, {dt:.1f} s on 1 host thread",
+            "cpu": cpu_model()}
+
+
+def cpu_baselines_per_config(budget_s: float) -> dict:
+    """The one-thread oracle on every workload the GPU path is measured on;
+    the two large ones on a bounded sample of their images."""
+    out = {}
+    for name, maker, sample in (("tiny_fp32", workloads.tiny, None),
+                                ("deit_s_80pct", workloads.deit_s, None),
+                                ("deit_b_sweep_B4_p80", lambda: workloads.deit_b_sweep(4, 0.8), None),
+                                ("deit_b_384_50pct", workloads.deit_b_384, 2),
+                                ("large_batch_threshold_l2", workloads.large_batch, 16)):
+        out[name] = cpu_baseline(maker(), budget_s, sample)
+        print(f"[bench] CPU oracle {name}: {out[name]['value']} images/s on 1 thread", flush=True)
+    return out
+
+
+def _oracle_worker_main(maker: str, budget_s: float) -> None:
+    """Entry of one all-cores worker process: prints 'reps seconds'."""
+    reps, dt = _oracle_loop(workloads.by_name(maker), budget_s)
+    print(f"{reps} {dt}", flush=True)
+
+
 def cpu_baseline_all_cores(w, maker: str, budget_s: float, max_procs: int = 16) -> dict:
-    """The CPU oracle on every host core at once: one worker process per core
-    (at most max_procs, the host share of one GPU), each running the
-    one-thread loop of cpu_baseline for the budget; images per second summed
-    over the workers.  Workers are started fresh (spawn): none touches the
-    GPU."""
-    import concurrent.futures
-    import multiprocessing
-    procs = max(1, min(max_procs, os.cpu_count() or 1))
-    ctx = multiprocessing.get_context("spawn")
-    with concurrent.futures.ProcessPoolExecutor(max_workers=procs, mp_context=ctx) as ex:
-        runs = list(ex.map(_oracle_batches, [maker] * procs, [budget_s] * procs))
+    """The CPU oracle on every usable host core at once: one plain child
+    process per core (at most max_procs, the host share of one GPU), each
+    running the one-thread loop of cpu_baseline for the budget; images per
+    second summed over the workers.  The children are started as fresh
+    interpreters that never touch the GPU, and all of them are waited for, so
+    none outlives the run."""
+    import subprocess
+    procs = max(1, min(max_procs, cpu_model()["usable_cpus"]))
+    code = ("import sys; sys.path.insert(0, %r); import bench; "
+            "bench._oracle_worker_main(%r, %r)" % (ROOT, maker, float(budget_s)))
+    env = {**os.environ, "OMP_NUM_THREADS": "1"}
+    children = [subprocess.Popen([sys.executable, "-c", code], stdout=subprocess.PIPE, text=True,
+                                 env=env, cwd=ROOT) for _ in range(procs)]
+    runs = []
+    for c in children:
+        out, _ = c.communicate()
+        if c.returncode != 0:
+            raise RuntimeError(f"oracle worker failed with status {c.returncode}")
+        reps, dt = out.split()[-2:]
+        runs.append((int(reps), float(dt)))
     rate = sum(reps * w.B / dt for reps, dt in runs)
     batches = sum(reps for reps, _ in runs)
     return {"value": round(rate, 2), "unit": "seqs/s", "cores": procs, "kind": "oracle",
             "sample": f"{batches} full batch(es) of the {w.name} workload (B={w.B}) through the "
                       f"fp64 oracle's scan, pack, attention and unpack, {procs} worker "
-                      f"process(es) of one thread for {budget_s:.0f} s each"}
+                      f"process(es) of one thread for {budget_s:.0f} s each",
+            "cpu": cpu_model()}
 
 
 def main():
@@ -773,6 +877,8 @@ def main():
                          "counters of the attention loop), then exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the traffic summary of two counter runs, then exit")
+    ap.add_argument("--peaks-only", action="store_true",
+                    help="only the box-peak probes (MFMA, exp2, fma), printed as JSON, then exit")
     ap.add_argument("--stack-only", choices=sorted(STACK_WORKLOADS),
                     help="only the three-call step, the layer stacks and the re-pack of one "
                          "workload (for a kernel trace of those kernels), then exit")
@@ -793,6 +899,9 @@ def main():
         return
     if args.pmc_forward:
         pmc_forward(args.pmc_forward)
+        return
+    if args.peaks_only:
+        print(json.dumps({"box_peaks": box_peaks(torch.cuda.current_stream())}), flush=True)
         return
     if args.stack_only:
         rattn_init()
@@ -883,6 +992,7 @@ def main():
     if not args.quick and not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
         line["cpu_baseline_all_cores"] = cpu_baseline_all_cores(w, "deit_s", args.cpu_budget)
+        line["cpu_baseline_per_config"] = cpu_baselines_per_config(args.cpu_budget / 3)
     print(json.dumps(line), flush=True)
 
 

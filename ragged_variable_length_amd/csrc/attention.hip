@@ -1062,37 +1062,38 @@ __global__ __launch_bounds__(kThreads) void fused32(const float *__restrict__ q,
 }
 
 template <typename T, int W, int QB>
-void launch_fwd16(const AttnArgs &a, float c, hipStream_t s) {
+hipError_t launch_fwd16(const AttnArgs &a, float c, hipStream_t s) {
     const int G = tile_groups(a.B, a.H, a.max_seqlen, 16 * W * QB, false);
     const unsigned grid = (unsigned)grid_for(a.B, a.H, G);
-    hipLaunchKernelGGL((attn_fwd16<T, W, QB>), dim3(grid), dim3(64 * W), 0, s,
-                       (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v,
-                       (uint16_t *)a.o, a.cu, a.B, a.H, G, a.max_seqlen, c);
+    return launch<attn_fwd16<T, W, QB>>(dim3(grid), dim3(64 * W), s, (const uint16_t *)a.q,
+                                        (const uint16_t *)a.k, (const uint16_t *)a.v,
+                                        (uint16_t *)a.o, a.cu, a.B, a.H, G, a.max_seqlen, c);
 }
 
 template <typename T>
-void launch_fwd16_shape(const AttnArgs &a, float c, hipStream_t s) {
+hipError_t launch_fwd16_shape(const AttnArgs &a, float c, hipStream_t s) {
     const Shape sh = shape_for(a.max_seqlen);
-    if (sh.QB == 1) launch_fwd16<T, 4, 1>(a, c, s);
-    else launch_fwd16<T, 4, 2>(a, c, s);
+    if (sh.QB == 1) return launch_fwd16<T, 4, 1>(a, c, s);
+    return launch_fwd16<T, 4, 2>(a, c, s);
 }
 
 template <typename T, int W, int QB>
-void launch_fused16(const FusedArgs &a, float c, hipStream_t s) {
+hipError_t launch_fused16(const FusedArgs &a, float c, hipStream_t s) {
     // without the padded output only tile 0 (the CLS row) is computed
     const int G = a.out ? tile_groups(a.B, a.H, std::min(a.max_seqlen, a.N), 16 * W * QB, true) : 1;
     const unsigned grid = (unsigned)grid_for(a.B, a.H, G);
-    hipLaunchKernelGGL((fused16<T, W, QB>), dim3(grid), dim3(64 * W), 0, s,
-                       (const uint16_t *)a.q, (const uint16_t *)a.k, (const uint16_t *)a.v, a.keep,
-                       (uint16_t *)a.out, (uint16_t *)a.cls, a.B, a.N, a.H, G, a.pad, c);
+    return launch<fused16<T, W, QB>>(dim3(grid), dim3(64 * W), s, (const uint16_t *)a.q,
+                                     (const uint16_t *)a.k, (const uint16_t *)a.v, a.keep,
+                                     (uint16_t *)a.out, (uint16_t *)a.cls, a.B, a.N, a.H, G, a.pad,
+                                     c);
 }
 
 template <typename T>
-void launch_fused16_shape(const FusedArgs &a, float c, hipStream_t s) {
+hipError_t launch_fused16_shape(const FusedArgs &a, float c, hipStream_t s) {
     // the CLS-only mode computes one tile per head: the smallest workgroup
     const Shape sh = a.out ? shape_for(std::min(a.max_seqlen, a.N)) : Shape{4, 1};
-    if (sh.QB == 1) launch_fused16<T, 4, 1>(a, c, s);
-    else launch_fused16<T, 4, 2>(a, c, s);
+    if (sh.QB == 1) return launch_fused16<T, 4, 1>(a, c, s);
+    return launch_fused16<T, 4, 2>(a, c, s);
 }
 
 }  // namespace
@@ -1100,34 +1101,32 @@ void launch_fused16_shape(const FusedArgs &a, float c, hipStream_t s) {
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s) {
     const float c = a.scale * kLog2e;
     switch (a.dt) {
-    case Elem::BF16: launch_fwd16_shape<__bf16>(a, c, s); break;
-    case Elem::F16: launch_fwd16_shape<_Float16>(a, c, s); break;
+    case Elem::BF16: return launch_fwd16_shape<__bf16>(a, c, s);
+    case Elem::F16: return launch_fwd16_shape<_Float16>(a, c, s);
     case Elem::F32: {
         const int G = tile_groups(a.B, a.H, a.max_seqlen, kQT, false);
-        hipLaunchKernelGGL(attn_fwd32, dim3((unsigned)grid_for(a.B, a.H, G)), dim3(kThreads), 0, s,
-                           (const float *)a.q, (const float *)a.k, (const float *)a.v,
-                           (float *)a.o, a.cu, a.B, a.H, G, a.max_seqlen, c);
-        break;
+        return launch<attn_fwd32>(dim3((unsigned)grid_for(a.B, a.H, G)), dim3(kThreads), s,
+                                  (const float *)a.q, (const float *)a.k, (const float *)a.v,
+                                  (float *)a.o, a.cu, a.B, a.H, G, a.max_seqlen, c);
     }
     }
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_fused(const FusedArgs &a, hipStream_t s) {
     const float c = a.scale * kLog2e;
     switch (a.dt) {
-    case Elem::BF16: launch_fused16_shape<__bf16>(a, c, s); break;
-    case Elem::F16: launch_fused16_shape<_Float16>(a, c, s); break;
+    case Elem::BF16: return launch_fused16_shape<__bf16>(a, c, s);
+    case Elem::F16: return launch_fused16_shape<_Float16>(a, c, s);
     case Elem::F32: {
         // without the padded output only tile 0 (the CLS row) is computed
         const int G = a.out ? tile_groups(a.B, a.H, std::min(a.max_seqlen, a.N), kQT, true) : 1;
-        hipLaunchKernelGGL(fused32, dim3((unsigned)grid_for(a.B, a.H, G)), dim3(kThreads), 0, s,
-                           (const float *)a.q, (const float *)a.k, (const float *)a.v, a.keep,
-                           (float *)a.out, (float *)a.cls, a.B, a.N, a.H, G, a.pad, c);
-        break;
+        return launch<fused32>(dim3((unsigned)grid_for(a.B, a.H, G)), dim3(kThreads), s,
+                               (const float *)a.q, (const float *)a.k, (const float *)a.v, a.keep,
+                               (float *)a.out, (float *)a.cls, a.B, a.N, a.H, G, a.pad, c);
     }
     }
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 }  // namespace rattn

@@ -9,7 +9,8 @@
 //   * empty-kernel launch + hipStreamSynchronize: the platform's floor;
 //   * rattn_forward + sync, the whole pack -> forward -> unpack step + sync, and
 //     the one-launch rattn_fused + sync;
-//   * the same step replayed from a captured hipGraph + sync;
+//   * the same step replayed from a captured hipGraph + sync, and the graph
+//     launch's own enqueue cost;
 //   * enqueue-only cost of the calls (no sync inside the timed span);
 //   * a stack of attention layers on one keep mask: packed once, attended per
 //     layer, unpacked once (section on the integrated packing pipeline: the
@@ -238,6 +239,41 @@ int bench_graph_floor(const bench_step *a, int what, int iters, int warmup, benc
         auto t1 = clk::now();
         if (i >= warmup) t.push_back(std::chrono::duration<double, std::micro>(t1 - t0).count());
     }
+    (void)hipGraphExecDestroy(ge);
+    (void)hipGraphDestroy(g);
+    if (rc == 0) summarize(t, out);
+    return rc;
+}
+
+// Host time of hipGraphLaunch alone for the same captured call(s), no sync
+// inside the timed span (the stream is drained every 64 launches outside it):
+// the graph's own enqueue cost, next to bench_enqueue_cost's direct calls.
+int bench_graph_enqueue_cost(const bench_step *a, int what, int iters, bench_stats *out) {
+    hipStream_t s = (hipStream_t)a->stream;
+    if (!s) return -3;
+    hipGraph_t g = nullptr;
+    hipGraphExec_t ge = nullptr;
+    if (hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal) != hipSuccess) return -1;
+    rattn_status st = run(a, what);
+    if (hipStreamEndCapture(s, &g) != hipSuccess || st != RATTN_OK) return -2;
+    if (hipGraphInstantiate(&ge, g, nullptr, nullptr, 0) != hipSuccess) return -1;
+    std::vector<double> t;
+    t.reserve(iters);
+    int rc = 0;
+    for (int i = 0; i < iters; ++i) {
+        auto t0 = clk::now();
+        if (hipGraphLaunch(ge, s) != hipSuccess) {
+            rc = -1;
+            break;
+        }
+        auto t1 = clk::now();
+        t.push_back(std::chrono::duration<double, std::micro>(t1 - t0).count());
+        if ((i & 63) == 63 && hipStreamSynchronize(s) != hipSuccess) {
+            rc = -1;
+            break;
+        }
+    }
+    if (hipStreamSynchronize(s) != hipSuccess) rc = -1;
     (void)hipGraphExecDestroy(ge);
     (void)hipGraphDestroy(g);
     if (rc == 0) summarize(t, out);

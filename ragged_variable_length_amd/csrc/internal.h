@@ -6,7 +6,72 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <cstddef>
+#include <cstring>
+
 namespace rattn {
+
+// ---------------------------------------------------------------------------
+// Kernel launch.  The arguments are written straight into one kernel-argument
+// block, in the kernel's parameter layout (each parameter at its natural
+// alignment, in order), and the block goes to hipModuleLaunchKernel with the
+// kernel's hipFunction_t, resolved once per device by hipGetFuncBySymbol: no
+// per-call lookup of the kernel by its host address and no per-argument
+// marshalling in the runtime, the kind of launch stub the pages credit with
+// the lower dispatch floor (radpulse.milrad-way.com write-up, section on the
+// 40 us Triton kernel).  Built with RATTN_LAUNCH_GGL, the launchers take the
+// plain hipLaunchKernelGGL + hipGetLastError path instead (the CPU emulation
+// of these sources, and the comparison of the two paths).
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+constexpr size_t kMaxKernArgBytes = 512;
+
+template <typename T> struct same_type { typedef T type; };
+
+#if !defined(RATTN_LAUNCH_GGL)
+template <auto Kernel>
+hipFunction_t kernel_function() {
+    static std::atomic<hipFunction_t> fn[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    hipFunction_t f = fn[dev].load(std::memory_order_acquire);
+    if (!f) {
+        if (hipGetFuncBySymbol(&f, reinterpret_cast<const void *>(Kernel)) != hipSuccess)
+            return nullptr;
+        fn[dev].store(f, std::memory_order_release);
+    }
+    return f;
+}
+#endif
+
+template <auto Kernel, typename... P>
+hipError_t launch_with(void (*)(P...), dim3 grid, dim3 block, hipStream_t s,
+                       typename same_type<P>::type... args) {
+#if defined(RATTN_LAUNCH_GGL)
+    hipLaunchKernelGGL(Kernel, grid, block, 0, s, args...);
+    return hipGetLastError();
+#else
+    alignas(16) unsigned char blk[kMaxKernArgBytes];
+    size_t off = 0;
+    ((off = (off + alignof(P) - 1) & ~(alignof(P) - 1), std::memcpy(blk + off, &args, sizeof(P)),
+      off += sizeof(P)),
+     ...);
+    static_assert(((sizeof(P) + alignof(P)) + ... + 0) <= kMaxKernArgBytes, "kernel arguments");
+    hipFunction_t f = kernel_function<Kernel>();
+    if (!f) return hipErrorInvalidDeviceFunction;
+    void *extra[] = {HIP_LAUNCH_PARAM_BUFFER_POINTER, blk, HIP_LAUNCH_PARAM_BUFFER_SIZE, &off,
+                     HIP_LAUNCH_PARAM_END};
+    return hipModuleLaunchKernel(f, grid.x, grid.y, grid.z, block.x, block.y, block.z, 0, s,
+                                 nullptr, extra);
+#endif
+}
+
+// launch<kernel>(grid, block, stream, arguments...): one enqueue, no sync.
+template <auto Kernel, typename... A>
+hipError_t launch(dim3 grid, dim3 block, hipStream_t s, A... args) {
+    return launch_with<Kernel>(Kernel, grid, block, s, args...);
+}
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));

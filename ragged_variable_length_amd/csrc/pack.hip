@@ -358,17 +358,12 @@ template <int NT>
 hipError_t launch_pack_nt(const PackArgs &a, hipStream_t s) {
     const int64_t tokens = (int64_t)a.B * a.N;
     const int64_t wgs = (int64_t)a.B * a.ch.nchunks;
-    if (tokens <= kSelfScanMaxTokens) {
-        hipLaunchKernelGGL((pack_kernel<true, NT>), dim3((unsigned)(wgs + 1)), dim3(kPackThreads),
-                           0, s, a);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a.keep, a.B, a.N, a.cu,
-                       a.max_out, a.total_out);
-    hipError_t e = hipGetLastError();
+    if (tokens <= kSelfScanMaxTokens)
+        return launch<pack_kernel<true, NT>>(dim3((unsigned)(wgs + 1)), dim3(kPackThreads), s, a);
+    hipError_t e = launch<scan_kernel>(dim3(1), dim3(kScanThreads), s, a.keep, a.B, a.N, a.cu,
+                                       a.max_out, a.total_out);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((pack_kernel<false, NT>), dim3((unsigned)wgs), dim3(kPackThreads), 0, s, a);
-    return hipGetLastError();
+    return launch<pack_kernel<false, NT>>(dim3((unsigned)wgs), dim3(kPackThreads), s, a);
 }
 
 }  // namespace
@@ -389,8 +384,7 @@ hipError_t launch_unpack(const UnpackArgs &a, hipStream_t s) {
         b.ch.chunk = 1;
     }
     const int64_t wgs = (int64_t)b.B * b.ch.nchunks;
-    hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)wgs), dim3(kPackThreads), 0, s, b);
-    return hipGetLastError();
+    return launch<unpack_kernel>(dim3((unsigned)wgs), dim3(kPackThreads), s, b);
 }
 
 }  // namespace rattn

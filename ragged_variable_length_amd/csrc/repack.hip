@@ -106,12 +106,11 @@ hipError_t launch_repack(const RepackArgs &args, hipStream_t s) {
     a.slices = (int)std::min<int64_t>(16, std::max<int64_t>(1, (512 + (int64_t)a.B - 1) / a.B));
     const dim3 grid((unsigned)((int64_t)a.B * a.slices)), block(kRepackThreads);
     switch (a.n_tensors) {
-        case 1: hipLaunchKernelGGL(repack_kernel<1>, grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL(repack_kernel<2>, grid, block, 0, s, a); break;
-        case 3: hipLaunchKernelGGL(repack_kernel<3>, grid, block, 0, s, a); break;
+        case 1: return launch<repack_kernel<1>>(grid, block, s, a);
+        case 2: return launch<repack_kernel<2>>(grid, block, s, a);
+        case 3: return launch<repack_kernel<3>>(grid, block, s, a);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace rattn

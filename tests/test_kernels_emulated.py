@@ -42,8 +42,10 @@ def emu_lib(tmp_path_factory):
     if not os.path.exists(CLANG) or rt is None:
         pytest.skip("clang++ with the AddressSanitizer runtime is not installed")
     out = str(tmp_path_factory.mktemp("emu") / "librattn_emu.so")
+    # RATTN_LAUNCH_GGL: the emulated runtime runs a kernel as a function call
+    # (hipLaunchKernelGGL), not through a device function handle
     cmd = [CLANG, "-std=c++20", "-O1", "-g", "-fPIC", "-shared", "-fsanitize=address",
-           "-shared-libasan", "-fno-omit-frame-pointer", "-w",
+           "-shared-libasan", "-fno-omit-frame-pointer", "-w", "-DRATTN_LAUNCH_GGL",
            "-I", os.path.join(HERE, "emu"), "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            "-x", "c++", os.path.join(HERE, "emu", "emu_runtime.cpp"),
            os.path.join(CSRC, "api.hip"), os.path.join(CSRC, "pack.hip"),
