@@ -115,6 +115,9 @@ def measured_traffic(workload: str):
 
 
 PMC_WORKLOADS = ("deit_s", "deit_b_384", "large_batch")
+# workloads whose rattn_forward launches are counted too (the attention alone
+# on flat buffers, against attention_bytes)
+PMC_FORWARD_WORKLOADS = ("deit_b_384", "large_batch")
 
 
 def summarize_pmc(fetch_csv: str, write_csv: str) -> str:
@@ -130,12 +133,14 @@ def summarize_pmc(fetch_csv: str, write_csv: str) -> str:
         copies = [float(r["Counter_Value"]) for r in rows
                   if "copyBuffer" in r["Kernel_Name"] and int(r["Grid_Size"]) > 100000]
         fused = [float(r["Counter_Value"]) for r in rows if "fused16" in r["Kernel_Name"]]
-        return copies, fused
+        fwd = [float(r["Counter_Value"]) for r in rows if "attn_fwd16" in r["Kernel_Name"]]
+        return copies, fused, fwd
 
     copy_bytes = 64 * 1024 * 1024 * 4
-    fc, ff = per_kernel(fetch_csv, "FETCH_SIZE")
-    wc, wf = per_kernel(write_csv, "WRITE_SIZE")
-    if len(ff) != 3 * len(PMC_WORKLOADS) or len(wf) != len(ff) or not fc or not wc:
+    fc, ff, fwf = per_kernel(fetch_csv, "FETCH_SIZE")
+    wc, wf, fww = per_kernel(write_csv, "WRITE_SIZE")
+    if (len(ff) != 3 * len(PMC_WORKLOADS) or len(wf) != len(ff) or not fc or not wc
+            or len(fwf) != 3 * len(PMC_FORWARD_WORKLOADS) or len(fww) != len(fwf)):
         raise RuntimeError("unexpected dispatches in the counter files")
     f_scale = copy_bytes / 1024.0 / (sum(fc) / len(fc))
     w_scale = copy_bytes / 1024.0 / (sum(wc) / len(wc))
@@ -151,13 +156,22 @@ def summarize_pmc(fetch_csv: str, write_csv: str) -> str:
         traffic = int(round((fk * f_scale + wk * w_scale) * 1024.0))
         out.append(f"{w.name} fetch_kib {fk:.2f} write_kib {wk:.2f} traffic_bytes {traffic} "
                    f"algorithmic_bytes {alg} ratio {traffic / alg:.3f}")
+    for i, name in enumerate(PMC_FORWARD_WORKLOADS):
+        w = workloads.by_name(name)
+        alg = attention_bytes(w.total_kept, w.H, w.dtype)
+        fk = sum(fwf[3 * i:3 * i + 3]) / 3.0
+        wk = sum(fww[3 * i:3 * i + 3]) / 3.0
+        traffic = int(round((fk * f_scale + wk * w_scale) * 1024.0))
+        out.append(f"forward_{w.name} fetch_kib {fk:.2f} write_kib {wk:.2f} traffic_bytes "
+                   f"{traffic} algorithmic_bytes {alg} ratio {traffic / alg:.3f}")
     return "\n".join(out) + "\n"
 
 
 def pmc_target() -> None:
     """Launches for the traffic counters (run under rocprofv3 --pmc): a plain
     256 MiB device copy for calibration, then three rattn_fused launches on
-    each of the DeiT-S 80 %, DeiT-B 384 px and batch-512 workloads."""
+    each of the DeiT-S 80 %, DeiT-B 384 px and batch-512 workloads, and three
+    rattn_forward launches on the flat buffers of the last two."""
     rattn_init()
     stream = torch.cuda.current_stream()
     src = torch.randn(64 * 1024 * 1024, device="cuda")
@@ -175,6 +189,15 @@ def pmc_target() -> None:
         print(f"[pmc] {r.w.name}: rattn_fused x3, algorithmic bytes "
               f"{fused_bytes(r.T, r.w.B, r.w.N, r.w.H, r.w.dtype)}", flush=True)
         del r
+    for name in PMC_FORWARD_WORKLOADS:
+        f = FlatResident(workloads.by_name(name), stream)
+        step = f.c_step()
+        if timing_lib().bench_loop(ctypes.byref(step), WHAT_FORWARD, 3) != 0:
+            raise RuntimeError("bench_loop(rattn_forward) failed")
+        torch.cuda.synchronize()
+        print(f"[pmc] {f.w.name}: rattn_forward x3, algorithmic bytes "
+              f"{attention_bytes(f.w.total_kept, f.w.H, f.w.dtype)}", flush=True)
+        del f
 
 
 def pmc_forward(name: str) -> None:
@@ -596,7 +619,7 @@ def forward_alone(w, stream, launches: int, flush_buf, cold_launches: int) -> di
     cold = times[len(times) // 2]
     T = int(f.cu[-1].item())
     nbytes = attention_bytes(T, w.H, w.dtype)
-    out = {"bytes": nbytes}
+    out = {"bytes": nbytes, "traffic_bytes": measured_traffic("forward_" + w.name)}
     for name, us in (("warm", warm), ("cold", cold)):
         gbs = nbytes / (us * 1e-6) / 1e9
         out[name] = {"us": round(us, 2), "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}

@@ -49,7 +49,7 @@ def test_attention_bytes():
     assert bench.attention_bytes(10, 12, "bf16") == 4 * 10 * 12 * 64 * 2
 
 
-def _write_counter_csv(path, counter, copy_kib, fused_kib):
+def _write_counter_csv(path, counter, copy_kib, fused_kib, fwd_kib=()):
     cols = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
     with open(path, "w", newline="") as f:
         w = csv.DictWriter(f, fieldnames=cols)
@@ -63,6 +63,10 @@ def _write_counter_csv(path, counter, copy_kib, fused_kib):
             w.writerow({"Dispatch_Id": d, "Kernel_Name": "rattn::fused16<__bf16, 4, 2>",
                         "Grid_Size": 196608, "Counter_Name": counter, "Counter_Value": v})
             d += 1
+        for v in fwd_kib:
+            w.writerow({"Dispatch_Id": d, "Kernel_Name": "rattn::attn_fwd16<__bf16, 4, 2>",
+                        "Grid_Size": 589824, "Counter_Name": counter, "Counter_Value": v})
+            d += 1
 
 
 def test_pmc_summary_scales_by_the_copy(tmp_path, monkeypatch):
@@ -73,11 +77,14 @@ def test_pmc_summary_scales_by_the_copy(tmp_path, monkeypatch):
     copy_kib = 64 * 1024 * 1024 * 4 / 1024
     n = len(bench.PMC_WORKLOADS)
     # FETCH_SIZE reads half of the copy's bytes (scale 2), WRITE_SIZE all of them
+    nf = len(bench.PMC_FORWARD_WORKLOADS)
     fetch = [float(10 * (i + 1)) for i in range(3 * n)]
     write = [float(5 * (i + 1)) for i in range(3 * n)]
+    ffetch = [float(7 * (i + 1)) for i in range(3 * nf)]
+    fwrite = [float(3 * (i + 1)) for i in range(3 * nf)]
     fp, wp = tmp_path / "fetch.csv", tmp_path / "write.csv"
-    _write_counter_csv(fp, "FETCH_SIZE", [copy_kib / 2] * 3, fetch)
-    _write_counter_csv(wp, "WRITE_SIZE", [copy_kib] * 3, write)
+    _write_counter_csv(fp, "FETCH_SIZE", [copy_kib / 2] * 3, fetch, ffetch)
+    _write_counter_csv(wp, "WRITE_SIZE", [copy_kib] * 3, write, fwrite)
     lines = bench.summarize_pmc(str(fp), str(wp)).splitlines()
     assert lines[0] == f"kernel_source_sha256 {bench.kernel_source_hash()}"
     assert lines[1] == "fetch_scale 2.0000" and lines[2] == "write_scale 1.0000"
@@ -88,6 +95,14 @@ def test_pmc_summary_scales_by_the_copy(tmp_path, monkeypatch):
         traffic = int(round((2 * fk + wk) * 1024))
         assert lines[3 + i] == (f"wl_{name} fetch_kib {fk:.2f} write_kib {wk:.2f} traffic_bytes "
                                 f"{traffic} algorithmic_bytes {alg} ratio {traffic / alg:.3f}")
+    alg = bench.attention_bytes(4, 1, "bf16")
+    for i, name in enumerate(bench.PMC_FORWARD_WORKLOADS):
+        fk = sum(ffetch[3 * i:3 * i + 3]) / 3
+        wk = sum(fwrite[3 * i:3 * i + 3]) / 3
+        traffic = int(round((2 * fk + wk) * 1024))
+        assert lines[3 + n + i] == (f"forward_wl_{name} fetch_kib {fk:.2f} write_kib {wk:.2f} "
+                                    f"traffic_bytes {traffic} algorithmic_bytes {alg} "
+                                    f"ratio {traffic / alg:.3f}")
 
 
 def test_pmc_summary_rejects_missing_dispatches(tmp_path):
