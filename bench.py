@@ -229,7 +229,10 @@ class BenchStats(ctypes.Structure):
 class BenchPeaks(ctypes.Structure):
     """bench_peaks_result of bench_peaks.hip."""
     _fields_ = [("mfma_bf16_tflops", ctypes.c_double), ("fma_exp_per_s", ctypes.c_double),
-                ("exp_per_s", ctypes.c_double), ("fma_f32_tflops", ctypes.c_double)]
+                ("exp_per_s", ctypes.c_double), ("fma_f32_tflops", ctypes.c_double),
+                ("mfma_ns", ctypes.c_double), ("mfma_exp_ns", ctypes.c_double),
+                ("split_mixed_s", ctypes.c_double), ("split_mfma_s", ctypes.c_double),
+                ("split_valu_s", ctypes.c_double)]
 
 
 class BenchStep(ctypes.Structure):
@@ -731,12 +734,20 @@ def box_peaks(stream, grid: int = 1024, iters: int = 2048) -> dict:
     res = BenchPeaks()
     if timing_lib().bench_peaks(grid, iters, stream.cuda_stream, ctypes.byref(res)) != 0:
         raise RuntimeError("bench_peaks failed")
+    # co-issue: half the wavefronts of each launch alone are half its time
+    mf, va, mix = res.split_mfma_s / 2, res.split_valu_s / 2, res.split_mixed_s
     return {"mfma_bf16_TFLOPs": round(res.mfma_bf16_tflops, 1),
             "fma_exp2_per_s": float(f"{res.fma_exp_per_s:.4g}"),
             "exp2_per_s": float(f"{res.exp_per_s:.4g}"),
             "fma_f32_TFLOPs": round(res.fma_f32_tflops, 1),
-            "from": "bench_peaks.hip: 1024 workgroups x 256 threads, 2048 iterations of eight "
-                    "independent chains per lane, HIP events around one launch after a warm-up"}
+            "mfma_ns_per_simd": round(res.mfma_ns, 2),
+            "mfma_plus_exp2_same_wave_ns_per_simd": round(res.mfma_exp_ns, 2),
+            "mfma_beside_valu_waves": {"mixed_ms": round(mix * 1e3, 3), "mfma_half_ms": round(mf * 1e3, 3),
+                                       "valu_half_ms": round(va * 1e3, 3),
+                                       "hidden_frac_of_smaller": round((mf + va - mix) / min(mf, va), 3)},
+            "from": "bench_peaks.hip: 1024 workgroups x 256 threads (split probes: 512 x 512), "
+                    "2048 iterations of eight independent chains per lane, HIP events around one "
+                    "launch after a warm-up"}
 
 
 def roofs_us(nbytes: int, flops: int, box_gbs, peaks) -> dict:
