@@ -47,9 +47,13 @@
  *     bitwise-identical results.  The opt-in debug-validate mode
  *     (rattn_set_validate) checks the bound and the shape of cu_seqlens with a
  *     device-to-host read before launching.
- *   - Thread safety: entry points may be called from several threads; the
- *     only global state is the one-time device check of rattn_init and the
- *     debug-validate flag.
+ *   - Thread safety: entry points may be called from several threads, on
+ *     the same or different streams; the only global state is the one-time
+ *     device check of rattn_init, the debug-validate flag, and a per-device
+ *     table of kernel handles that each kernel's first launch on a device
+ *     fills (atomically; a racing second lookup stores the same handle).
+ *     No call keeps anything on the device between calls, so calls on
+ *     different streams share nothing but their arguments.
  */
 #ifndef RATTN_H
 #define RATTN_H
