@@ -654,44 +654,70 @@ def padded_comparison(r: Resident, launches: int, rounds: int = 3) -> dict:
     return out
 
 
+def config_report(w, stream, launches: int, cold_launches: int, flush, box_gbs=None,
+                  peaks=None) -> dict:
+    """One workload on its own: rattn_fused warm and cold with its bytes,
+    flops, measured traffic (when the counter profile covers it) and lower
+    bounds; the dense comparator; the three-call step and the layer stacks;
+    rattn_forward alone."""
+    r = Resident(w, stream)
+    nbytes = fused_bytes(r.T, w.B, w.N, w.H, w.dtype)
+    flops = attention_flops(r.lengths, w.H)
+    row = {"B": w.B, "N": w.N, "H": w.H, "dtype": w.dtype, "T": r.T,
+           "fused_bytes": nbytes, "attn_flops": flops,
+           "traffic_bytes": measured_traffic(w.name),
+           "roofs_us": roofs_us(nbytes, flops, box_gbs, peaks)}
+    row["padded_comparator"] = padded_comparison(r, launches)
+    row["three_call_and_stacks"] = three_call_and_stacks(r, launches)
+    row["forward_alone"] = forward_alone(w, stream, launches, flush, cold_launches)
+    for cold in (False, True):
+        us = kernel_time_us(r, launches, cold, flush, cold_launches)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        tfl = flops / (us * 1e-6) / 1e12
+        row["cold" if cold else "warm"] = {
+            "us": round(us, 2), "seqs_per_s": round(w.B / (us * 1e-6), 1),
+            "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "TFLOPs": round(tfl, 2), "mfma_frac": round(tfl / MFMA_PEAK_TFLOPS[w.dtype], 4)}
+    pc = row["padded_comparator"]
+    print(f"[bench] {w.name}: warm {row['warm']['us']} us ({row['warm']['hbm_frac']:.3f} of HBM),"
+          f" cold {row['cold']['us']} us ({row['cold']['hbm_frac']:.3f}); padded comparator "
+          f"{pc['padded_longest_us']} us (longest survivor) / {pc['padded_n_us']} us (N)",
+          flush=True)
+    _print_stacks(w.name, row["three_call_and_stacks"])
+    fa = row["forward_alone"]
+    print(f"[bench] {w.name}: rattn_forward alone warm {fa['warm']['us']} us "
+          f"({fa['warm']['hbm_frac']:.3f} of HBM), cold {fa['cold']['us']} us "
+          f"({fa['cold']['hbm_frac']:.3f})", flush=True)
+    del r
+    return row
+
+
 def large_configs(stream, launches: int, cold_launches: int, box_gbs=None, peaks=None) -> dict:
     out = {}
     flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device="cuda")
     for name, maker in (("deit_b_384_50pct", workloads.deit_b_384),
                         ("large_batch_threshold_l2", workloads.large_batch)):
-        w = maker()
-        r = Resident(w, stream)
-        nbytes = fused_bytes(r.T, w.B, w.N, w.H, w.dtype)
-        flops = attention_flops(r.lengths, w.H)
-        row = {"B": w.B, "N": w.N, "H": w.H, "dtype": w.dtype, "T": r.T,
-               "fused_bytes": nbytes, "attn_flops": flops,
-               "traffic_bytes": measured_traffic(w.name),
-               "roofs_us": roofs_us(nbytes, flops, box_gbs, peaks)}
-        row["padded_comparator"] = padded_comparison(r, launches)
-        row["three_call_and_stacks"] = three_call_and_stacks(r, launches)
-        row["forward_alone"] = forward_alone(w, stream, launches, flush, cold_launches)
-        for cold in (False, True):
-            us = kernel_time_us(r, launches, cold, flush, cold_launches)
-            gbs = nbytes / (us * 1e-6) / 1e9
-            tfl = flops / (us * 1e-6) / 1e12
-            row["cold" if cold else "warm"] = {
-                "us": round(us, 2), "seqs_per_s": round(w.B / (us * 1e-6), 1),
-                "GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                "TFLOPs": round(tfl, 2), "mfma_frac": round(tfl / MFMA_PEAK_TFLOPS[w.dtype], 4)}
-        out[name] = row
-        pc = row["padded_comparator"]
-        print(f"[bench] {name}: warm {row['warm']['us']} us ({row['warm']['hbm_frac']:.3f} of HBM),"
-              f" cold {row['cold']['us']} us ({row['cold']['hbm_frac']:.3f}); padded comparator "
-              f"{pc['padded_longest_us']} us (longest survivor) / {pc['padded_n_us']} us (N)",
-              flush=True)
-        _print_stacks(name, row["three_call_and_stacks"])
-        fa = row["forward_alone"]
-        print(f"[bench] {name}: rattn_forward alone warm {fa['warm']['us']} us "
-              f"({fa['warm']['hbm_frac']:.3f} of HBM), cold {fa['cold']['us']} us "
-              f"({fa['cold']['hbm_frac']:.3f})", flush=True)
-        del r
+        out[name] = config_report(maker(), stream, launches, cold_launches, flush, box_gbs, peaks)
     del flush
     return out
+
+
+def config_workload(spec: str, seed):
+    """--config: tiny, deit_s, deit_b_384, large_batch, or deit_b_sweep:B:p
+    (B images, pruning fraction p; p = exact for the unpruned point)."""
+    name, *rest = spec.split(":")
+    if name == "deit_b_sweep":
+        if len(rest) != 2:
+            raise SystemExit("--config deit_b_sweep:B:p, e.g. deit_b_sweep:4:0.8")
+        exact = rest[1] == "exact"
+        return workloads.deit_b_sweep(int(rest[0]), 0.0 if exact else float(rest[1]), seed=seed,
+                                      exact_unpruned=exact)
+    if rest:
+        raise SystemExit(f"--config {name} takes no parameters")
+    try:
+        return workloads.by_name(name, seed=seed)
+    except KeyError:
+        raise SystemExit(f"unknown --config {name}") from None
 
 
 STACK_WORKLOADS = {"deit_s_80pct": workloads.deit_s, "deit_b_384_50pct": workloads.deit_b_384,
@@ -911,6 +937,11 @@ def main():
                          "counters of the attention loop), then exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the traffic summary of two counter runs, then exit")
+    ap.add_argument("--config", metavar="NAME",
+                    help="time one workload on its own (tiny, deit_s, deit_b_384, large_batch, "
+                         "deit_b_sweep:B:p) and print its report as one JSON line, then exit")
+    ap.add_argument("--seed", type=int, default=None,
+                    help="with --config: the workload's seed (default: its fixed seed)")
     ap.add_argument("--peaks-only", action="store_true",
                     help="only the box-peak probes (MFMA, exp2, fma), printed as JSON, then exit")
     ap.add_argument("--stack-only", choices=sorted(STACK_WORKLOADS),
@@ -944,6 +975,15 @@ def main():
         t = three_call_and_stacks(Resident(w, stream), 200)
         _print_stacks(w.name, t)
         print(json.dumps({"workload": w.name, "three_call_and_stacks": t}), flush=True)
+        return
+    if args.config:
+        w = config_workload(args.config, args.seed)
+        rattn_init()
+        stream = torch.cuda.current_stream()
+        flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device="cuda")
+        row = config_report(w, stream, 300, 50, flush)
+        print(json.dumps({"config": args.config, "workload": w.name, "seed": w.seed,
+                          "data": "synthetic", **row}), flush=True)
         return
     rattn_init()
     stream = torch.cuda.current_stream()

@@ -223,3 +223,22 @@ def test_attention_flops_reproduce_the_pages_reduction_at_80pct_pruning():
         assert round(reduction, 2) == flops["attention_flop_reduction"], (after, reduction)
     # and the closed form (1 - p)^2 of the kept fraction
     assert round(1.0 - (1.0 - flops["prune_rate"]) ** 2, 2) == flops["attention_flop_reduction"]
+
+
+def test_config_workload_names():
+    """bench.py --config: every configuration by name, sweep points with their
+    parameters, an explicit seed, and clear errors for malformed names."""
+    cases = {"tiny": ("tiny", 4, 197, 3, "f32"), "deit_s": ("deit_s_80pct", 32, 197, 6, "f16"),
+             "deit_b_384": ("deit_b_384_50pct", 64, 577, 12, "bf16"),
+             "large_batch": ("large_batch_threshold_l2", 512, 197, 6, "bf16"),
+             "deit_b_sweep:4:0.8": ("deit_b_sweep_B4_p80", 4, 197, 12, "bf16"),
+             "deit_b_sweep:1:exact": ("deit_b_sweep_B1_unpruned_exact", 1, 197, 12, "bf16")}
+    for spec, (name, B, N, H, dt) in cases.items():
+        w = bench.config_workload(spec, None)
+        assert (w.name, w.B, w.N, w.H, w.dtype) == (name, B, N, H, dt), spec
+    a = bench.config_workload("deit_s", 123)
+    b = bench.config_workload("deit_s", 124)
+    assert a.seed == 123 and a.kept_counts != b.kept_counts
+    for bad in ("nope", "deit_s:3", "deit_b_sweep:4"):
+        with pytest.raises(SystemExit):
+            bench.config_workload(bad, None)
