@@ -24,7 +24,7 @@ from tests._gpu_util import (CANARY, FLAT_TOL, UNIT_ROUNDOFF, bits, check_indexi
                              check_padded, run_hip, say)
 
 pytestmark = pytest.mark.gpu
-N_CASES = 24
+N_CASES = 64
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -38,9 +38,9 @@ def _device():
 def _draw(seed):
     g = np.random.default_rng(10_000 + seed)
     dtype = ["bf16", "f16", "f32"][int(g.integers(3))]
-    N = int(g.choice([1, 7, 40, 64, 65, 130, 197, 257, 300, 577]))
-    B = int(g.integers(1, 24 if N <= 300 else 8))
-    H = int(g.integers(1, 9 if dtype != "f32" else 5))
+    N = int(g.choice([1, 7, 40, 64, 65, 130, 197, 257, 300, 577, 1100, 2048]))
+    B = int(g.integers(1, 24 if N <= 300 else (8 if N <= 577 else 3)))
+    H = int(g.integers(1, (9 if dtype != "f32" else 5) if N <= 577 else 3))
     scale = 0.125 if g.random() < 0.7 else float(g.choice([0.03, 0.2, -0.05, 0.0]))
     keep = torch.zeros((B, N), dtype=torch.uint8)
     tg = torch.Generator().manual_seed(20_000 + seed)
