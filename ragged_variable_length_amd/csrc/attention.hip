@@ -313,6 +313,21 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
         if constexpr (QB == 1) return i;
         else return (i < nreal && (((tile * kQT16) >> 8) & 1)) ? nreal - 1 - i : i;
     };
+    // Tile order.  Several workgroups per head: tiles g, g+G, ...  One
+    // workgroup per head with 128-row tiles: within each pair of 256-row
+    // blocks the tiles go 0, 2, 1, 3, so that every tile after the first
+    // starts with the two chunks the previous one ended with (the blocks
+    // take the chunks in opposite orders), still in the double buffer.
+    auto next_tile_of = [&](int tile) {
+        if (QB == 1 || G != 1) return tile + G;
+        constexpr int kOrder[4] = {0, 2, 1, 3};
+        const int base = tile & ~3, pos = tile & 3;
+        int i = 0;
+        while (kOrder[i] != pos) ++i;
+        for (++i; i < 4; ++i)
+            if (base + kOrder[i] < ntile) return base + kOrder[i];
+        return base + 4;  // next group (tile 0 of it, or past the end)
+    };
     int t = g, idx = 0, step = 0;
     int ch = chunk_at(t, 0);
     int buf = resident ? ch : 0;
@@ -358,7 +373,7 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
     while (true) {
         int nt = t, ni = idx + 1;
         if (ni == nch) {
-            nt = t + G;
+            nt = next_tile_of(t);
             ni = 0;
         }
         const bool has_next = nt < ntile;
