@@ -664,6 +664,64 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
     }
 }
 
+// One 32-key chunk of the float32 online softmax for the 16 query rows of a
+// wavefront: the chunk's scores S^T = K Q^T (keys at or past `valid` masked),
+// the running row maximum m and row sum, and O^T += V^T P^T.  Ks and Vs hold
+// the chunk's K and V rows in LDS at a pitch of kLd32 floats; qf[kk] is the B
+// operand Q[query col][4*kk + grp].  acc_j[i] is O^T[16*j + 4*grp + i][col].
+__device__ __forceinline__ void step32(const float *Ks, const float *Vs, const float (&qf)[16],
+                                       int valid, float c, float &m, float &lsum, f32x4 &acc0,
+                                       f32x4 &acc1, f32x4 &acc2, f32x4 &acc3) {
+    const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[col * kLd32 + 4 * kk + grp], qf[kk], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[(16 + col) * kLd32 + 4 * kk + grp], qf[kk], s1, 0, 0, 0);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float x0 = s0[i] * c, x1 = s1[i] * c;
+        if (4 * grp + i >= valid) x0 = -INFINITY;
+        if (16 + 4 * grp + i >= valid) x1 = -INFINITY;
+        s0[i] = x0;
+        s1[i] = x1;
+        mx = fmaxf(mx, fmaxf(x0, x1));
+    }
+    mx = max_across_groups(mx);
+    const float mn = fmaxf(m, mx);
+    const float alpha = fast_exp2(m - mn);
+    m = mn;
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        s0[i] = fast_exp2(s0[i] - mn);
+        s1[i] = fast_exp2(s1[i] - mn);
+        ps += s0[i] + s1[i];
+    }
+    lsum = lsum * alpha + ps;
+    acc0 *= alpha;
+    acc1 *= alpha;
+    acc2 *= alpha;
+    acc3 *= alpha;
+    // O^T += V^T P^T, one key per 16x16x4 step: lane group g supplies key
+    // 16*blk + 4*g + i, which is exactly the score it holds in slot i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float *v0 = Vs + (4 * grp + i) * kLd32 + col;
+        const float *v1 = Vs + (16 + 4 * grp + i) * kLd32 + col;
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(v0[0], s0[i], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(v0[16], s0[i], acc1, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(v0[32], s0[i], acc2, 0, 0, 0);
+        acc3 = __builtin_amdgcn_mfma_f32_16x16x4f32(v0[48], s0[i], acc3, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(v1[0], s1[i], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(v1[16], s1[i], acc1, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(v1[32], s1[i], acc2, 0, 0, 0);
+        acc3 = __builtin_amdgcn_mfma_f32_16x16x4f32(v1[48], s1[i], acc3, 0, 0, 0);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // float32 core: the 64-query tiles g, g+G, ... of one (image, head), 32-key
 // chunks
@@ -729,56 +787,8 @@ __device__ __forceinline__ void attend32(const float *__restrict__ q, const floa
             const int buf = ch & 1;
             const bool more = stage && ch + 1 < nch;
             if (more) RATTN_LOAD32(ch + 1)
-            const float *Ks = sK + buf * (kKC32 * kLd32);
-            const float *Vs = sV + buf * (kKC32 * kLd32);
-            f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
-#pragma unroll
-            for (int kk = 0; kk < 16; ++kk) {
-                s0 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[col * kLd32 + 4 * kk + grp], qf[kk], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_16x16x4f32(Ks[(16 + col) * kLd32 + 4 * kk + grp], qf[kk], s1, 0, 0, 0);
-            }
-            const int valid = L - ch * kKC32;
-            float mx = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float x0 = s0[i] * c, x1 = s1[i] * c;
-                if (4 * grp + i >= valid) x0 = -INFINITY;
-                if (16 + 4 * grp + i >= valid) x1 = -INFINITY;
-                s0[i] = x0;
-                s1[i] = x1;
-                mx = fmaxf(mx, fmaxf(x0, x1));
-            }
-            mx = max_across_groups(mx);
-            const float mn = fmaxf(m, mx);
-            const float alpha = fast_exp2(m - mn);
-            m = mn;
-            float ps = 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                s0[i] = fast_exp2(s0[i] - mn);
-                s1[i] = fast_exp2(s1[i] - mn);
-                ps += s0[i] + s1[i];
-            }
-            lsum = lsum * alpha + ps;
-            acc0 *= alpha;
-            acc1 *= alpha;
-            acc2 *= alpha;
-            acc3 *= alpha;
-            // O^T += V^T P^T, one key per 16x16x4 step: lane group g supplies key
-            // 16*blk + 4*g + i, which is exactly the score it holds in slot i
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float *v0 = Vs + (4 * grp + i) * kLd32 + col;
-                const float *v1 = Vs + (16 + 4 * grp + i) * kLd32 + col;
-                acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(v0[0], s0[i], acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(v0[16], s0[i], acc1, 0, 0, 0);
-                acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(v0[32], s0[i], acc2, 0, 0, 0);
-                acc3 = __builtin_amdgcn_mfma_f32_16x16x4f32(v0[48], s0[i], acc3, 0, 0, 0);
-                acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(v1[0], s1[i], acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(v1[16], s1[i], acc1, 0, 0, 0);
-                acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(v1[32], s1[i], acc2, 0, 0, 0);
-                acc3 = __builtin_amdgcn_mfma_f32_16x16x4f32(v1[48], s1[i], acc3, 0, 0, 0);
-            }
+            step32(sK + buf * (kKC32 * kLd32), sV + buf * (kKC32 * kLd32), qf,
+                   L - ch * kKC32, c, m, lsum, acc0, acc1, acc2, acc3);
             if (more) RATTN_STORE32(buf ^ 1)
             __syncthreads();
         }
@@ -803,6 +813,112 @@ __device__ __forceinline__ void attend32(const float *__restrict__ q, const floa
     }
 #undef RATTN_LOAD32
 #undef RATTN_STORE32
+}
+
+// ---------------------------------------------------------------------------
+// float32 core for batches of few heads: the 16-query tiles g, g+G, ... of one
+// (image, head).  Wavefront w takes the tile's 32-key chunks w, w+4, ... into
+// an LDS slab of its own, so a short sequence's chunks run on four SIMDs at
+// once instead of one after another.  The four partial softmax states (row
+// maximum, row sum, unnormalised output) are then merged in LDS in wavefront
+// order 0, 1, 2, 3, whatever order the wavefronts finished in.
+// ---------------------------------------------------------------------------
+constexpr int kSlab32 = 2 * kKC32 * kLd32;  // floats: one chunk of K and of V
+
+template <typename Rows>
+__device__ __forceinline__ void attend32_split(const float *__restrict__ q,
+                                               const float *__restrict__ k,
+                                               const float *__restrict__ v, float *__restrict__ o,
+                                               const Rows &R, int L, int Lp, float c, int g, int G,
+                                               float *slabs, float *__restrict__ cls_dst) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    float *sK = slabs + wid * kSlab32, *sV = sK + kKC32 * kLd32;
+    // a chunk is 32 keys x 16 four-float vectors per tensor; lane l copies
+    // vector l & 15 of keys (l >> 4) + 4 j, j = 0..7
+    const int c4 = lane & 15, key0 = lane >> 4;
+    u32x4 kr[8], vr[8];
+    auto load = [&](int ch) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int key = ch * kKC32 + key0 + 4 * j;
+            kr[j] = zero4;
+            vr[j] = zero4;
+            if (key < L) {
+                kr[j] = *(const u32x4 *)(k + R.off(key) + 4 * c4);
+                vr[j] = *(const u32x4 *)(v + R.off(key) + 4 * c4);
+            }
+        }
+    };
+    const int nch = (Lp + kKC32 - 1) / kKC32;
+    const int ntile = (Lp + kQW - 1) / kQW;
+    for (int t = g; t < ntile; t += G) {
+        // every wavefront has read the previous tile's partial states
+        if (t != g) __syncthreads();
+        const int qrow = t * kQW + col;
+        float qf[16];
+        {
+            const float *src = q + (qrow < L ? R.off(qrow) : 0u);
+#pragma unroll
+            for (int kk = 0; kk < 16; ++kk) qf[kk] = qrow < L ? src[4 * kk + grp] : 0.f;
+        }
+        // finite, so that a chunk with no valid key (padded length) leaves
+        // the state unchanged instead of giving exp2(-inf + inf)
+        float m = -__FLT_MAX__, lsum = 0.f;
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, acc2 = acc0, acc3 = acc0;
+        if (wid < nch) load(wid);
+        for (int ch = wid; ch < nch; ch += kWaves) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                *(u32x4 *)(sK + (key0 + 4 * j) * kLd32 + 4 * c4) = kr[j];
+                *(u32x4 *)(sV + (key0 + 4 * j) * kLd32 + 4 * c4) = vr[j];
+            }
+            // LDS serves one wavefront's instructions in order: the slab is
+            // written before this wavefront's reads below, and read before
+            // its next writes
+            __builtin_amdgcn_wave_barrier();
+            if (ch + kWaves < nch) load(ch + kWaves);
+            step32(sK, sV, qf, L - ch * kKC32, c, m, lsum, acc0, acc1, acc2, acc3);
+            __builtin_amdgcn_wave_barrier();
+        }
+        // partial state into the own slab: output block j at 256 j + 4 lane,
+        // then the 16 row maxima and the 16 row sums
+        lsum = sum_across_groups(lsum);
+        *(f32x4 *)(sK + 4 * lane) = acc0;
+        *(f32x4 *)(sK + 256 + 4 * lane) = acc1;
+        *(f32x4 *)(sK + 512 + 4 * lane) = acc2;
+        *(f32x4 *)(sK + 768 + 4 * lane) = acc3;
+        if (grp == 0) {
+            sK[1024 + col] = m;
+            sK[1040 + col] = lsum;
+        }
+        __syncthreads();
+        // wavefront w merges output block w (dimensions 16 w .. 16 w + 15)
+        float mw[kWaves], lw[kWaves];
+        f32x4 aw[kWaves];
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float *part = slabs + w * kSlab32;
+            mw[w] = part[1024 + col];
+            lw[w] = part[1040 + col];
+            aw[w] = *(const f32x4 *)(part + 256 * wid + 4 * lane);
+        }
+        const float M = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
+        float l = 0.f;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = fast_exp2(mw[w] - M);
+            l += f * lw[w];
+            acc += f * aw[w];
+        }
+        const float inv = 1.f / l;
+        if (qrow < L) {
+            if (o) *(f32x4 *)(o + R.off(qrow) + 16 * wid + 4 * grp) = acc * inv;
+            if (cls_dst && qrow == 0) *(f32x4 *)(cls_dst + 16 * wid + 4 * grp) = acc * inv;
+        }
+    }
 }
 
 // (image, head, tile group) of this workgroup; false if the id is padding.
@@ -837,10 +953,10 @@ __device__ __forceinline__ bool decode_group(int BH, int H, int G, int *b, int *
 // 60.3 us.
 constexpr int64_t kComputeUnits = 256;
 
-int tile_groups(int B, int H, int max_seqlen, int rows, bool spare_for_zeros) {
+int tile_groups(int B, int H, int max_seqlen, int rows, bool spare_for_zeros, int per_cu = 1) {
     const int ntiles = max_seqlen > 0 ? (max_seqlen + rows - 1) / rows : 1;
     const int64_t pairs = std::max<int64_t>((int64_t)B * H, 1);
-    int64_t G = kComputeUnits / pairs;
+    int64_t G = per_cu * kComputeUnits / pairs;
     if (spare_for_zeros && pairs < kComputeUnits) G = std::max<int64_t>(G, 2);
     if (!spare_for_zeros && rows == 128) G = std::max<int64_t>(G, std::min(ntiles, 3));
     return (int)std::max<int64_t>(1, std::min<int64_t>(G, std::max(ntiles, spare_for_zeros ? 2 : 1)));
@@ -863,6 +979,24 @@ Shape shape_for(int max_seqlen) {
     // a 64-image batch run in one round
     if (max_seqlen <= 256) return Shape{4, 1};
     return Shape{4, 2};
+}
+
+// The float32 path splits each tile's keys over its four wavefronts
+// (attend32_split) when the batch has at most this many heads.  The rule
+// reads B and H only, never the length bound, so every entry point picks the
+// same core for the same batch and their outputs stay bitwise equal.
+constexpr int64_t kSplit32Heads = 64;
+bool split32(int B, int H) { return (int64_t)B * H <= kSplit32Heads; }
+// Workgroups per head of the split core (16-row tiles).  One per CU while
+// that runs at least half of each head's tiles under the bound at once; else
+// up to two per CU, which their 70 KB of LDS leave room for.  Measured on
+// float32 batches of 197 positions, half kept (rattn_fused): 24 heads 7.7 us
+// with one per CU against 9.8 with two (two split workgroups sharing a CU's
+// SIMDs), 48 heads 12.1 against 10.1.
+int split32_groups(int B, int H, int bound, bool spare_for_zeros) {
+    const int ntiles = bound > 0 ? (bound + kQW - 1) / kQW : 1;
+    const int one = tile_groups(B, H, bound, kQW, spare_for_zeros);
+    return 2 * one >= ntiles ? one : tile_groups(B, H, bound, kQW, spare_for_zeros, 2);
 }
 
 int64_t grid_for(int B, int H, int G) { return 8 * (((int64_t)B * H + 7) / 8) * G; }
@@ -898,14 +1032,14 @@ __global__ __launch_bounds__(64 * W, QB == 1 ? 4 : 3) void attn_fwd16(const uint
                                   sV, sQ, nullptr);
 }
 
+template <bool SPLIT>
 __global__ __launch_bounds__(kThreads) void attn_fwd32(const float *__restrict__ q,
                                                        const float *__restrict__ k,
                                                        const float *__restrict__ v,
                                                        float *__restrict__ o,
                                                        const int32_t *__restrict__ cu, int B,
                                                        int H, int G, int max_seqlen, float c) {
-    __shared__ __attribute__((aligned(16))) float sK[2 * kKC32 * kLd32];
-    __shared__ __attribute__((aligned(16))) float sV[2 * kKC32 * kLd32];
+    __shared__ __attribute__((aligned(16))) float lds[SPLIT ? kWaves * kSlab32 : 2 * kSlab32];
     int b, h, g;
     if (!decode_group(B * H, H, G, &b, &h, &g)) return;
     const int seq0 = cu[b];
@@ -914,7 +1048,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd32(const float *__restrict__
     const int64_t rs = (int64_t)H * kD;
     const int64_t base = (int64_t)seq0 * rs + (int64_t)h * kD;
     const FlatRows R = {(uint32_t)rs};
-    attend32(q + base, k + base, v + base, o + base, R, L, L, c, g, G, sK, sV, nullptr);
+    if (SPLIT)
+        attend32_split(q + base, k + base, v + base, o + base, R, L, L, c, g, G, lds, nullptr);
+    else
+        attend32(q + base, k + base, v + base, o + base, R, L, L, c, g, G, lds, lds + kSlab32,
+                 nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -1033,6 +1171,7 @@ __global__ __launch_bounds__(64 * W, QB == 1 ? 4 : 3) void fused16(const uint16_
                                          rs * 2 / 16, (u32x4 *)cls_head);
 }
 
+template <bool SPLIT>
 __global__ __launch_bounds__(kThreads) void fused32(const float *__restrict__ q,
                                                     const float *__restrict__ k,
                                                     const float *__restrict__ v,
@@ -1040,8 +1179,7 @@ __global__ __launch_bounds__(kThreads) void fused32(const float *__restrict__ q,
                                                     float *__restrict__ out,
                                                     float *__restrict__ cls, int B, int N,
                                                     int H, int G, int pad, float c) {
-    __shared__ __attribute__((aligned(16))) float sK[2 * kKC32 * kLd32];
-    __shared__ __attribute__((aligned(16))) float sV[2 * kKC32 * kLd32];
+    __shared__ __attribute__((aligned(16))) float lds[SPLIT ? kWaves * kSlab32 : 2 * kSlab32];
     __shared__ int16_t pos[kMaxFusedN];
     __shared__ uint64_t keep_bits[kMaxFusedN / 64];
     int b, h, g;
@@ -1062,12 +1200,15 @@ __global__ __launch_bounds__(kThreads) void fused32(const float *__restrict__ q,
             // CLS rows only: the workgroup holding query tile 0 computes that
             // tile alone
             run = cls_dst && g == 0;
-            GG = (Lp + kQT - 1) / kQT;
+            GG = (Lp + (SPLIT ? kQW : kQT) - 1) / (SPLIT ? kQW : kQT);
             gg = 0;
         }
-        if (run)
-            attend32(q + head0, k + head0, v + head0, out_head, R, L, Lp, c, gg, GG, sK, sV,
-                     cls_dst);
+        if (run && SPLIT)
+            attend32_split(q + head0, k + head0, v + head0, out_head, R, L, Lp, c, gg, GG, lds,
+                           cls_dst);
+        else if (run)
+            attend32(q + head0, k + head0, v + head0, out_head, R, L, Lp, c, gg, GG, lds,
+                     lds + kSlab32, cls_dst);
     }
     // zeros for the pruned rows: by the last workgroup of the head, after its
     // attention
@@ -1119,10 +1260,17 @@ hipError_t launch_attention(const AttnArgs &a, hipStream_t s) {
     case Elem::BF16: return launch_fwd16_shape<__bf16>(a, c, s);
     case Elem::F16: return launch_fwd16_shape<_Float16>(a, c, s);
     case Elem::F32: {
-        const int G = tile_groups(a.B, a.H, a.max_seqlen, kQT, false);
-        return launch<attn_fwd32>(dim3((unsigned)grid_for(a.B, a.H, G)), dim3(kThreads), s,
-                                  (const float *)a.q, (const float *)a.k, (const float *)a.v,
-                                  (float *)a.o, a.cu, a.B, a.H, G, a.max_seqlen, c);
+        const bool split = split32(a.B, a.H);
+        const int G = split ? split32_groups(a.B, a.H, a.max_seqlen, false)
+                            : tile_groups(a.B, a.H, a.max_seqlen, kQT, false);
+        const dim3 grid((unsigned)grid_for(a.B, a.H, G));
+        if (split)
+            return launch<attn_fwd32<true>>(grid, dim3(kThreads), s, (const float *)a.q,
+                                            (const float *)a.k, (const float *)a.v, (float *)a.o,
+                                            a.cu, a.B, a.H, G, a.max_seqlen, c);
+        return launch<attn_fwd32<false>>(grid, dim3(kThreads), s, (const float *)a.q,
+                                         (const float *)a.k, (const float *)a.v, (float *)a.o,
+                                         a.cu, a.B, a.H, G, a.max_seqlen, c);
     }
     }
     return hipErrorInvalidValue;
@@ -1134,11 +1282,21 @@ hipError_t launch_fused(const FusedArgs &a, hipStream_t s) {
     case Elem::BF16: return launch_fused16_shape<__bf16>(a, c, s);
     case Elem::F16: return launch_fused16_shape<_Float16>(a, c, s);
     case Elem::F32: {
+        const bool split = split32(a.B, a.H);
         // without the padded output only tile 0 (the CLS row) is computed
-        const int G = a.out ? tile_groups(a.B, a.H, std::min(a.max_seqlen, a.N), kQT, true) : 1;
-        return launch<fused32>(dim3((unsigned)grid_for(a.B, a.H, G)), dim3(kThreads), s,
-                               (const float *)a.q, (const float *)a.k, (const float *)a.v, a.keep,
-                               (float *)a.out, (float *)a.cls, a.B, a.N, a.H, G, a.pad, c);
+        const int bound = std::min(a.max_seqlen, a.N);
+        const int G = !a.out ? 1
+                      : split ? split32_groups(a.B, a.H, bound, true)
+                              : tile_groups(a.B, a.H, bound, kQT, true);
+        const dim3 grid((unsigned)grid_for(a.B, a.H, G));
+        if (split)
+            return launch<fused32<true>>(grid, dim3(kThreads), s, (const float *)a.q,
+                                         (const float *)a.k, (const float *)a.v, a.keep,
+                                         (float *)a.out, (float *)a.cls, a.B, a.N, a.H, G, a.pad,
+                                         c);
+        return launch<fused32<false>>(grid, dim3(kThreads), s, (const float *)a.q,
+                                      (const float *)a.k, (const float *)a.v, a.keep,
+                                      (float *)a.out, (float *)a.cls, a.B, a.N, a.H, G, a.pad, c);
     }
     }
     return hipErrorInvalidValue;

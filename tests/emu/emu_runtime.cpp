@@ -3,6 +3,7 @@
 #include "hip/hip_runtime.h"
 thread_local emu_idx threadIdx, blockIdx;
 thread_local dim3 blockDim, gridDim;
+thread_local unsigned emu_phase;
 EmuBlock *g_emu;
 void emu_launch(dim3 grid, dim3 block, const std::function<void()> &body) {
     const int nt = block.x;
@@ -10,7 +11,7 @@ void emu_launch(dim3 grid, dim3 block, const std::function<void()> &body) {
     std::vector<std::barrier<> *> wb;
     for (int w = 0; w < nt / 64; ++w) wb.push_back(new std::barrier<>(64));
     EmuBlock e; e.nthreads = nt; e.block_bar = &bb; e.wave_bar = wb;
-    e.slot.assign(nt / 64, std::vector<uint64_t>(64));
+    e.slot.assign(nt / 64, std::vector<uint64_t>(128));
     g_emu = &e;
     std::vector<std::thread> ts;
     for (int t = 0; t < nt; ++t)

@@ -41,9 +41,15 @@ struct EmuBlock {
     int nthreads;
     std::barrier<> *block_bar;
     std::vector<std::barrier<> *> wave_bar;
-    std::vector<std::vector<uint64_t>> slot;      // per wave, 64 lanes, generic 8-byte payload
+    std::vector<std::vector<uint64_t>> slot;      // per wave, 2 x 64 lanes, generic 8-byte payload
 };
 extern EmuBlock *g_emu;
+// Every lane of a wave makes the same sequence of wave exchanges, and each
+// exchange uses the slot set of its parity: a lane writes set n+1 only after
+// all lanes passed exchange n's barrier, i.e. finished reading set n-1, so one
+// barrier per exchange suffices.
+extern thread_local unsigned emu_phase;
+inline unsigned emu_next_set() { return 64u * ((emu_phase++) & 1u); }
 
 inline void __syncthreads() { g_emu->block_bar->arrive_and_wait(); }
 inline int emu_lane() { return threadIdx.x & 63; }
@@ -52,11 +58,11 @@ inline void emu_wave_sync() { g_emu->wave_bar[emu_wave()]->arrive_and_wait(); }
 
 template <typename T> inline T emu_exchange_get(T v, int src_lane) {
     static_assert(sizeof(T) <= 8, "");
+    const unsigned set = emu_next_set();
     uint64_t bits = 0; std::memcpy(&bits, &v, sizeof(T));
-    g_emu->slot[emu_wave()][emu_lane()] = bits;
+    g_emu->slot[emu_wave()][set + emu_lane()] = bits;
     emu_wave_sync();
-    uint64_t got = g_emu->slot[emu_wave()][src_lane & 63];
-    emu_wave_sync();
+    uint64_t got = g_emu->slot[emu_wave()][set + (src_lane & 63)];
     T r; std::memcpy(&r, &got, sizeof(T)); return r;
 }
 template <typename T> inline T __shfl_xor(T v, int m, int w = 64) { return emu_exchange_get(v, emu_lane() ^ m); }
@@ -64,11 +70,11 @@ template <typename T> inline T __shfl_up(T v, unsigned d, int w = 64) {
     int l = emu_lane(); return emu_exchange_get(v, l >= (int)d ? l - (int)d : l);
 }
 inline uint64_t __ballot(int pred) {
-    g_emu->slot[emu_wave()][emu_lane()] = pred ? 1 : 0;
+    const unsigned set = emu_next_set();
+    g_emu->slot[emu_wave()][set + emu_lane()] = pred ? 1 : 0;
     emu_wave_sync();
     uint64_t m = 0;
-    for (int i = 0; i < 64; ++i) if (g_emu->slot[emu_wave()][i]) m |= 1ull << i;
-    emu_wave_sync();
+    for (int i = 0; i < 64; ++i) if (g_emu->slot[emu_wave()][set + i]) m |= 1ull << i;
     return m;
 }
 inline int __popc(uint32_t x) { return __builtin_popcount(x); }
@@ -86,8 +92,8 @@ typedef _Float16 emu_f16x8 __attribute__((ext_vector_type(8)));
 template <int KP>
 inline emu_f32x4 emu_mfma16(const float *a, const float *b, emu_f32x4 c) {
     struct Ent { float a[8], b[8]; };
-    static Ent buf[16][64];  // per wave, per lane
-    Ent *w = buf[emu_wave()];
+    static Ent buf[16][128];  // per wave, two sets of 64 lanes
+    Ent *w = buf[emu_wave()] + emu_next_set();
     Ent &e = w[emu_lane()];
     for (int j = 0; j < KP; ++j) { e.a[j] = a[j]; e.b[j] = b[j]; }
     emu_wave_sync();
@@ -102,7 +108,6 @@ inline emu_f32x4 emu_mfma16(const float *a, const float *b, emu_f32x4 c) {
         }
         d[i] = (float)(c[i] + acc);
     }
-    emu_wave_sync();
     return d;
 }
 inline emu_f32x4 emu_mfma_bf16(emu_bf16x8 a, emu_bf16x8 b, emu_f32x4 c, int, int, int) {
@@ -131,15 +136,15 @@ typedef uint32_t emu_u32x2 __attribute__((ext_vector_type(2)));
 inline emu_u32x2 emu_permlane_swap(uint32_t old, uint32_t src, int width) {
     const uint32_t o_self = old, s_self = src;
     const int l = emu_lane();
-    g_emu->slot[emu_wave()][l] = ((uint64_t)s_self << 32) | o_self;
+    const unsigned set = emu_next_set();
+    g_emu->slot[emu_wave()][set + l] = ((uint64_t)s_self << 32) | o_self;
     emu_wave_sync();
-    auto o_at = [&](int i) { return (uint32_t)(g_emu->slot[emu_wave()][i] & 0xFFFFFFFFu); };
-    auto s_at = [&](int i) { return (uint32_t)(g_emu->slot[emu_wave()][i] >> 32); };
+    auto o_at = [&](int i) { return (uint32_t)(g_emu->slot[emu_wave()][set + i] & 0xFFFFFFFFu); };
+    auto s_at = [&](int i) { return (uint32_t)(g_emu->slot[emu_wave()][set + i] >> 32); };
     emu_u32x2 r;
     const bool upper = (l / width) & 1;  // odd block of `width` lanes
     r[0] = upper ? s_at(l - width) : o_at(l);
     r[1] = upper ? s_at(l) : o_at(l + width);
-    emu_wave_sync();
     return r;
 }
 #define __builtin_amdgcn_permlane32_swap(O, S, FI, BC) emu_permlane_swap((O), (S), 32)
@@ -174,17 +179,18 @@ inline void emu_global_load_lds(const void *g, void *lds, int size, int, int) {
 typedef short emu_s16x4 __attribute__((ext_vector_type(4)));
 inline emu_s16x4 emu_ds_read_tr16(const void *p) {
     const uint64_t addr = (uint64_t)(uintptr_t)p;
-    g_emu->slot[emu_wave()][emu_lane()] = addr;
+    const unsigned set = emu_next_set();
+    g_emu->slot[emu_wave()][set + emu_lane()] = addr;
     emu_wave_sync();
     const int l = emu_lane(), g0 = l & ~15, i = l & 15;
     emu_s16x4 r;
     for (int j = 0; j < 4; ++j) {
-        const short *w = (const short *)(uintptr_t)g_emu->slot[emu_wave()][g0 + 4 * j + i / 4];
+        const short *w = (const short *)(uintptr_t)g_emu->slot[emu_wave()][set + g0 + 4 * j + i / 4];
         r[j] = w[i % 4];
     }
-    emu_wave_sync();
     return r;
 }
 #define __builtin_amdgcn_ds_read_tr16_b64_v4i16(P) emu_ds_read_tr16((const void *)(P))
 #define __builtin_amdgcn_s_waitcnt(X) ((void)0)
 #define __builtin_amdgcn_sched_barrier(X) ((void)0)
+#define __builtin_amdgcn_wave_barrier() emu_wave_sync()

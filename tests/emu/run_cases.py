@@ -197,6 +197,26 @@ def case_padded():
               flush=True)
 
 
+def case_f32_sequential():
+    # float32 batches of more than 64 heads keep one wavefront per 16 query
+    # rows over all key chunks (fewer heads split the keys over the four
+    # wavefronts, which the other float32 cases run): 65 heads against the
+    # oracle, fused against the three calls and padded against fused, with
+    # empty, length-one and chunk-edge images
+    keep = _keep_lengths([1, 0, 33, 40, 17], 40, seed=60)
+    w = workloads.custom(5, 40, 13, "f32", keep=keep, seed=61, name="f32_5x13")
+    check_both(w)
+    ref_out, ref_cls = fused(w)
+    out = torch.empty_like(w.q)
+    cls = torch.empty((w.B, w.H, w.D), dtype=w.q.dtype)
+    for t in (out, cls):
+        t.view(torch.uint8).fill_(POISON)
+    rv.rattn_fused_padded(w.q, w.k, w.v, w.keep, w.scale, w.N, out_padded=out, cls=cls)
+    assert np.array_equal(U.bits(out), U.bits(ref_out)), (w.name, "padded out")
+    assert np.array_equal(U.bits(cls), U.bits(ref_cls)), (w.name, "padded cls")
+    print(f"{w.name}: padded to {w.N}: bits equal to ragged", flush=True)
+
+
 def repack_check(flat, keep2, cu, n_tensors=1, name="repack"):
     """rattn_repack on host tensors against the oracle: rows, cu_seqlens and
     total bit-exact, rows past T2 untouched."""
