@@ -21,9 +21,14 @@ EXT = os.path.join(HERE, "_rattn" + sysconfig.get_config_var("EXT_SUFFIX"))
 EXT_SOURCE = "pymod.c"
 
 # Device-code flags: gfx950 only; packed-fp32 instruction selection off (the
-# compiler would otherwise form v_pk_* float ops on its own).
+# compiler would otherwise form v_pk_* float ops on its own); kernel arguments
+# preloaded into SGPRs at wave launch (the first 14 dwords, gfx950 code object
+# v5), so a wavefront's first addresses do not wait for a scalar load of the
+# argument segment.  Each kernel keeps a prologue that loads them itself when
+# the firmware does not preload.  Measured on MI355X, rattn_fused at DeiT-S:
+# 5.90 -> 5.65 us warm, 9.24 -> 8.9-9.0 us cold, bits unchanged.
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
-                "-packed-fp32-ops"]
+                "-packed-fp32-ops", "-mllvm", "-amdgpu-kernarg-preload-count=16"]
 
 
 def hipcc() -> str:

@@ -18,17 +18,20 @@ import subprocess
 
 import pytest
 
+from ragged_variable_length_amd import build
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "ragged_variable_length_amd", "csrc")
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+# the product build's device flags, so the checked code is the shipped code
+DEVICE_FLAGS = build.DEVICE_FLAGS
 
 pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
 
 
 def _device_asm(src, tmp_path):
     out = tmp_path / (os.path.basename(src) + ".s")
-    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "--cuda-device-only", "-S",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    cmd = [HIPCC, *DEVICE_FLAGS, "-O3", "-std=c++17", "--cuda-device-only", "-S",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC, src, "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True, text=True, timeout=600)
     return out.read_text()
