@@ -1059,14 +1059,47 @@ __global__ __launch_bounds__(kThreads) void attn_fwd32(const float *__restrict__
 // fused kernels: padded in, padded out, one launch, one workgroup per
 // (image, head)
 // ---------------------------------------------------------------------------
-// Kept positions of image b, in order, into pos[]; returns the count.  Every
-// wavefront loads the mask bytes of its 64-position chunks (chunk c belongs to
-// wave c % W) in one round trip and ballots them; the ballots go to LDS as a
-// keep bitmap, and after one exchange of per-chunk counts each wavefront
-// writes its kept positions at their ranks.
+// Ranking an image of at most C 64-position chunks (N <= 64 C, C a multiple
+// of W): every wavefront loads and ballots all C chunks in one round trip and
+// counts the kept positions before each chunk in scalar registers;
+// wavefront w writes the positions and the keep bits of chunks w, w+W, ...,
+// and one barrier publishes them.
+template <int W, int C>
+__device__ __forceinline__ int rank_all(const uint8_t *__restrict__ keep_img, int N,
+                                        int16_t *pos, uint64_t *keep_bits) {
+    static_assert(C % W == 0, "chunks dealt evenly");
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nchunk = (N + 63) / 64;
+    uint8_t byte[C];
+#pragma unroll
+    for (int i = 0; i < C; ++i) byte[i] = keep_img[min(64 * i + lane, N - 1)];
+    int total = 0;  // kept positions before chunk i
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const bool kept = 64 * i + lane < N && byte[i] != 0;
+        const uint64_t m = __ballot(kept);
+        if (i % W == w && i < nchunk) {
+            if (kept) pos[total + __popcll(m & ((1ull << lane) - 1ull))] = (int16_t)(64 * i + lane);
+            if (lane == 0) keep_bits[i] = m;
+        }
+        total += __popcll(m);
+    }
+    __syncthreads();
+    return total;
+}
+
+// Kept positions of image b, in order, into pos[]; returns the count.  The
+// keep bitmap (one 64-bit ballot per 64-position chunk) goes to keep_bits.
+// Up to 1024 positions every wavefront ranks the whole image (rank_all);
+// longer images: chunk c belongs to wavefront c % W, the ballots go to LDS,
+// and after one exchange of per-chunk counts each wavefront writes its kept
+// positions at their ranks.
 template <int W>
 __device__ __forceinline__ int rank_image(const uint8_t *__restrict__ keep_img, int N,
                                           int16_t *pos, uint64_t *keep_bits) {
+    if (N <= 64 * W) return rank_all<W, W>(keep_img, N, pos, keep_bits);
+    if (N <= 1024) return rank_all<W, 16>(keep_img, N, pos, keep_bits);
     constexpr int kChunksPerWave = (kMaxFusedN + 64 * W - 1) / (64 * W);
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int nchunk = (N + 63) / 64;

@@ -269,6 +269,11 @@ def case_long():
     keep = _keep_lengths([100, 150, 200], 300, seed=52)
     check_both(workloads.custom(3, 300, 1, "bf16", keep=keep, seed=53, name="long_chunks_2_3_4"),
                flat=False)
+    # past 1024 positions the fused kernel ranks through an LDS exchange of
+    # per-chunk counts instead of in every wavefront
+    keep = _keep_lengths([90, 1025], 1025, seed=54)
+    check_both(workloads.custom(2, 1025, 1, "bf16", keep=keep, seed=55, name="long_1025_bf16"),
+               flat=False)
 
 
 def case_scan_large():

@@ -170,6 +170,18 @@ def test_fused_long_sequences(N):
     full(workloads.custom(2, N, 2, "bf16", keep=keep, seed=15, name=f"long_{N}"), flat=True)
 
 
+@pytest.mark.parametrize("N", [256, 257, 1024, 1025])
+def test_fused_rank_tiers(N):
+    # the mask is ranked by every wavefront up to 4 and up to 16 chunks of 64
+    # positions, through an LDS exchange past that: each side of both edges,
+    # with an image that keeps only its last position and one that keeps all
+    keep = _keep_length_range(4, N, 1, N // 3, seed=17 + N)
+    keep[1] = 0
+    keep[1, N - 1] = 1
+    keep[2] = 1
+    full(workloads.custom(4, N, 2, "bf16", keep=keep, seed=18 + N, name=f"rank_tier_{N}"))
+
+
 @pytest.mark.parametrize("B,N", [(1, 1), (3, 5), (700, 7)])
 def test_fused_small_rows(B, N):
     full(workloads.custom(B, N, 1, "bf16", p_keep=0.6, seed=16 + N, name=f"small_{B}x{N}"),
