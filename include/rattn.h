@@ -47,6 +47,15 @@
  *     bitwise-identical results.  The opt-in debug-validate mode
  *     (rattn_set_validate) checks the bound and the shape of cu_seqlens with a
  *     device-to-host read before launching.
+ *   - Order of the softmax accumulation: in a batch of few heads (B * H <= 24
+ *     for RATTN_BF16 / RATTN_F16, <= 64 for RATTN_F32) an image longer than
+ *     one key chunk (64 keys; every image for RATTN_F32) has its keys split
+ *     over four partial softmax states, merged in a fixed order; otherwise
+ *     each query row takes the keys in one sequence.  An image's output bits
+ *     can therefore differ, within rounding, between batches whose head counts
+ *     fall on different sides of those limits.  They never depend on the
+ *     other images' contents, the bound, the padded length or the entry point
+ *     (fused, three calls or padded comparator).
  *   - Thread safety: entry points may be called from several threads, on
  *     the same or different streams; the only global state is the one-time
  *     device check of rattn_init, the debug-validate flag, and a per-device

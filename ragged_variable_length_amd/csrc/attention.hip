@@ -196,7 +196,11 @@ __device__ __forceinline__ void wait_vmem_but() {
 // read from LDS, and their MFMA and softmax work is independent, so the
 // wavefront always has one block's arithmetic to overlap with the other's.
 // ---------------------------------------------------------------------------
-template <typename T, bool kPos, int W, int QB, typename Rows>
+// kTag only tells specializations apart: the kernels for batches of few heads
+// use attend16 with kTag = 1, the same code as the other kernels' kTag = 0
+// (the host compilation pass of ROCm 7.2 rejects one specialization called
+// from both kernel families).
+template <typename T, bool kPos, int W, int QB, typename Rows, int kTag = 0>
 __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
                                          const uint16_t *__restrict__ kh,
                                          const uint16_t *__restrict__ vh,
@@ -664,6 +668,219 @@ __device__ __forceinline__ void attend16(const uint16_t *__restrict__ qh,
     }
 }
 
+// ---------------------------------------------------------------------------
+// 16-bit core for batches of few heads: the 16-query tiles g, g+G, ... of one
+// (image, head).  Wavefront w takes the tile's 64-key chunks w, w+4, ...,
+// each copied by its own DMA into an LDS slab of its own (K and V in the
+// swizzled layout of attend16), so a short sequence's chunks run on four
+// SIMDs at once instead of one after another.  Per chunk the arithmetic is
+// attend16's for one block of 16 rows: S^T on the matrix cores, the lazy
+// per-row reference maximum, probabilities rounded to T, O^T and the row
+// sums on the matrix cores.  The four partial states (reference maximum,
+// row sum, unnormalised output) are then merged in LDS in wavefront order
+// 0, 1, 2, 3.  A chunk with no key inside the sequence (the padded
+// comparator's) is skipped, so padding changes nothing.
+// ---------------------------------------------------------------------------
+constexpr int kSlab16 = 2 * kKC * 64;  // 16-bit elements: one chunk of K and of V
+
+template <typename T, bool kPos, typename Rows>
+__device__ __forceinline__ void attend16_split(const uint16_t *__restrict__ qh,
+                                               const uint16_t *__restrict__ kh,
+                                               const uint16_t *__restrict__ vh,
+                                               uint16_t *__restrict__ oh, const Rows &R, int L,
+                                               int Lp, float c, int g, int G, uint16_t *slabs,
+                                               uint16_t *__restrict__ cls_dst) {
+    typedef typename Mma<T>::v8 V8;
+    constexpr uint32_t kOneBits = Mma<T>::kOnePair;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 15, grp = lane >> 4;
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    uint16_t *sK = slabs + wid * kSlab16, *sV = sK + kKC * 64;
+    float *part = (float *)sK;  // the partial state, once the chunks are done
+
+    // a chunk is 16 DMA instructions of 8 rows (1 KB): 8 for K, 8 for V;
+    // lane l fills row l/8, slot l%8 of each 8-row block.  Keys past the
+    // sequence end copy the last key's row (finite, masked or weighted 0).
+    const int srow = lane >> 3, sslot = lane & 7;
+    auto stage = [&](int chunk) {
+        uint32_t ro[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ro[i] = R.off(min(chunk * kKC + 8 * i + srow, L - 1));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = 8 * i + srow;
+            __builtin_amdgcn_global_load_lds(kh + ro[i] + 8 * kpiece(row, sslot),
+                                             RATTN_LDS(sK + 8 * i * 64), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vh + ro[i] + 8 * vpiece(row, sslot),
+                                             RATTN_LDS(sV + 8 * i * 64), 16, 0, 0);
+        }
+    };
+
+    const V8 ones = __builtin_bit_cast(V8, u32x4{kOneBits, kOneBits, kOneBits, kOneBits});
+    const int vr = 4 * grp + (col >> 2);
+    const int vp = (col & 3) >> 1, vhalf = 4 * (col & 1);
+    const float lag = kPos ? fminf(8.f / c, 3.4028234663852886e38f) : 0.f;
+    const int nch = (Lp + kKC - 1) / kKC;
+    const int ntile = (Lp + kQW - 1) / kQW;
+    for (int t = g; t < ntile; t += G) {
+        // every wavefront has read the previous tile's partial states
+        if (t != g) __syncthreads();
+        // B operand of S^T: query row t*16 + col, dims 8*grp.. and 32 + 8*grp..
+        const int qr = t * kQW + col;
+        u32x4 qf0 = zero4, qf1 = zero4;
+        if (qr < L) {
+            const uint16_t *src = qh + R.off(qr);
+            qf0 = *(const u32x4 *)(src + 8 * grp);
+            qf1 = *(const u32x4 *)(src + 32 + 8 * grp);
+        }
+        float m = -INFINITY, mc = -INFINITY;
+        f32x4 acc[4], accl = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) acc[dt] = accl;
+        for (int ch = wid; ch < nch; ch += kWaves) {
+            const int valid = L - ch * kKC;
+            if (valid <= 0) continue;
+            const int valid_p = Lp - ch * kKC;
+            // this wavefront's earlier reads of the slab are done before the
+            // copies overwrite it; the copies (and the Q rows) have landed
+            // before the reads below
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+            stage(ch);
+            wait_vmem();
+            __builtin_amdgcn_wave_barrier();
+            f32x4 s[4];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) {
+                const int row = 16 * blk + col;
+                const u32x4 a0 = *(const u32x4 *)(sK + row * 64 + 8 * kpiece(row, grp));
+                const u32x4 a1 = *(const u32x4 *)(sK + row * 64 + 8 * kpiece(row, 4 + grp));
+                f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                z = Mma<T>::run(__builtin_bit_cast(V8, a0), __builtin_bit_cast(V8, qf0), z);
+                s[blk] = Mma<T>::run(__builtin_bit_cast(V8, a1), __builtin_bit_cast(V8, qf1), z);
+                if constexpr (kPos) {
+                    const float t3 = vmax(vmax(s[blk][0], s[blk][1]), s[blk][2]);
+                    mx = vmax(vmax(mx, t3), s[blk][3]);
+                }
+            }
+            if constexpr (kPos) {
+                // the lazy reference of attend16: a row moves its reference
+                // (raw units) only when its own maximum passed it by the lag
+                if (__ballot(mx > m + lag)) {
+                    const float mxa = max_across_groups(mx);
+                    const bool row_grows = mxa > m + lag;
+                    const float alpha = row_grows ? fast_exp2((m - mxa) * c) : 1.f;
+                    m = row_grows ? mxa : m;
+                    mc = m * c;
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
+                    accl[0] *= alpha;
+                }
+            }
+            if (valid < kKC) {
+#pragma unroll
+                for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (16 * blk + 4 * grp + i >= valid) s[blk][i] = -INFINITY;
+            }
+            if constexpr (!kPos) {
+                // scale <= 0: scale, then the exact running maximum
+                float mxn = -INFINITY;
+#pragma unroll
+                for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float x = s[blk][i] == -INFINITY ? -INFINITY : s[blk][i] * c;
+                        s[blk][i] = x;
+                        mxn = fmaxf(mxn, x);
+                    }
+                mxn = max_across_groups(mxn);
+                const float mn = fmaxf(m, mxn);
+                const float alpha = m == mn ? 1.f : fast_exp2(m - mn);
+                const float mref = mn == -INFINITY ? 0.f : mn;
+                m = mn;
+#pragma unroll
+                for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) s[blk][i] = fast_exp2(s[blk][i] - mref);
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) acc[dt] *= alpha;
+                accl[0] *= alpha;
+            }
+            // O^T += V^T P^T and the row sums, in 32-key halves, as attend16
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                if (ks == 0 || valid_p > 32) {
+                    if constexpr (kPos) {
+#pragma unroll
+                        for (int blk = 2 * ks; blk < 2 * ks + 2; ++blk)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                s[blk][i] = fast_exp2(__builtin_fmaf(s[blk][i], c, -mc));
+                    }
+                    u32x4 pb;
+                    pb[0] = pack2<T>(s[2 * ks][0], s[2 * ks][1]);
+                    pb[1] = pack2<T>(s[2 * ks][2], s[2 * ks][3]);
+                    pb[2] = pack2<T>(s[2 * ks + 1][0], s[2 * ks + 1][1]);
+                    pb[3] = pack2<T>(s[2 * ks + 1][2], s[2 * ks + 1][3]);
+                    const V8 b = __builtin_bit_cast(V8, pb);
+                    const int r0 = 32 * ks + vr, r1 = r0 + 16;
+                    const uint16_t *v0 = sV + r0 * 64 + vhalf;
+                    const uint16_t *v1 = sV + r1 * 64 + vhalf;
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt) {
+                        const u32x2 lo = lds_read_tr(v0 + 8 * vpiece(r0, 2 * dt + vp));
+                        const u32x2 hi = lds_read_tr(v1 + 8 * vpiece(r1, 2 * dt + vp));
+                        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+                        acc[dt] = Mma<T>::run(__builtin_bit_cast(V8, a), b, acc[dt]);
+                    }
+                    accl = Mma<T>::run(ones, b, accl);
+                }
+            }
+        }
+        // partial state into the own slab: output block dt at 256 dt + 4 lane,
+        // then the 16 reference maxima and the 16 row sums
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the slab's reads are done
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) *(f32x4 *)(part + 256 * dt + 4 * lane) = acc[dt];
+        if (grp == 0) {
+            part[1024 + col] = m;
+            part[1040 + col] = accl[0];
+        }
+        __syncthreads();
+        // wavefront w merges output block w (dimensions 16 w .. 16 w + 15)
+        float mw[kWaves], lw[kWaves];
+        f32x4 aw[kWaves];
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float *pw = (const float *)(slabs + w * kSlab16);
+            mw[w] = pw[1024 + col];
+            lw[w] = pw[1040 + col];
+            aw[w] = *(const f32x4 *)(pw + 256 * wid + 4 * lane);
+        }
+        const float M = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
+        float l = 0.f;
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            // a wavefront with no valid chunk has reference -inf: weight 0
+            const float f = fast_exp2(kPos ? (mw[w] - M) * c : mw[w] - M);
+            l += f * lw[w];
+            o += f * aw[w];
+        }
+        const int qrow = t * kQW + col;
+        if (qrow < L) {
+            const float inv = __builtin_amdgcn_rcpf(l);
+            const u32x2 wv = {pack2<T>(o[0] * inv, o[1] * inv), pack2<T>(o[2] * inv, o[3] * inv)};
+            if (oh) *(u32x2 *)(oh + R.off(qrow) + 16 * wid + 4 * grp) = wv;
+            if (cls_dst && qrow == 0) *(u32x2 *)(cls_dst + 16 * wid + 4 * grp) = wv;
+        }
+    }
+}
+
 // One 32-key chunk of the float32 online softmax for the 16 query rows of a
 // wavefront: the chunk's scores S^T = K Q^T (keys at or past `valid` masked),
 // the running row maximum m and row sum, and O^T += V^T P^T.  Ks and Vs hold
@@ -981,19 +1198,21 @@ Shape shape_for(int max_seqlen) {
     return Shape{4, 2};
 }
 
-// The float32 path splits each tile's keys over its four wavefronts
-// (attend32_split) when the batch has at most this many heads.  The rule
-// reads B and H only, never the length bound, so every entry point picks the
-// same core for the same batch and their outputs stay bitwise equal.
+// Each path splits a tile's keys over its four wavefronts (attend32_split,
+// attend16_split) when the batch has at most this many heads.  The rule reads
+// B and H only, never the length bound, so every entry point picks the same
+// core for the same batch and their outputs stay bitwise equal.
 constexpr int64_t kSplit32Heads = 64;
+constexpr int64_t kSplit16Heads = 24;
 bool split32(int B, int H) { return (int64_t)B * H <= kSplit32Heads; }
-// Workgroups per head of the split core (16-row tiles).  One per CU while
-// that runs at least half of each head's tiles under the bound at once; else
-// up to two per CU, which their 70 KB of LDS leave room for.  Measured on
-// float32 batches of 197 positions, half kept (rattn_fused): 24 heads 7.7 us
-// with one per CU against 9.8 with two (two split workgroups sharing a CU's
-// SIMDs), 48 heads 12.1 against 10.1.
-int split32_groups(int B, int H, int bound, bool spare_for_zeros) {
+bool split16(int B, int H) { return (int64_t)B * H <= kSplit16Heads; }
+// Workgroups per head of a split core (16-row tiles).  One per CU while that
+// runs at least half of each head's tiles under the bound at once; else up to
+// two per CU, which their 68-74 KB of LDS leave room for.  Measured on float32
+// batches of 197 positions, half kept (rattn_fused): 24 heads 7.7 us with one
+// per CU against 9.8 with two (two split workgroups sharing a CU's SIMDs),
+// 48 heads 12.1 against 10.1.
+int split_groups(int B, int H, int bound, bool spare_for_zeros) {
     const int ntiles = bound > 0 ? (bound + kQW - 1) / kQW : 1;
     const int one = tile_groups(B, H, bound, kQW, spare_for_zeros);
     return 2 * one >= ntiles ? one : tile_groups(B, H, bound, kQW, spare_for_zeros, 2);
@@ -1204,6 +1423,96 @@ __global__ __launch_bounds__(64 * W, QB == 1 ? 4 : 3) void fused16(const uint16_
                                          rs * 2 / 16, (u32x4 *)cls_head);
 }
 
+// Kernels for batches of few heads.  The core for one (image, head) is
+// chosen by the image's kept count L, the same in every entry point whatever
+// the bound or the padded length: an image of one 64-key chunk has no keys
+// to split and runs attend16 on one 64-row tile, exactly as in a batch of
+// many heads; a longer one runs the key-split core on 16-row tiles.  The G
+// workgroups of a head are dealt 16-row tiles (g, g+G, ...); with 64-row
+// tiles only g = 0 has one.  attend16's two K and two V chunk buffers use
+// the first two slabs (its Q buffer serves two-block wavefronts only).
+#define RATTN_ATTEND_FEW(RT, QH, KH, VH, OH, R, L, LP, C, G_, GG, SLABS, CLS)                \
+    do {                                                                                    \
+        uint16_t *sK_ = (SLABS), *sV_ = (SLABS) + 2 * kKC * 64, *sQ_ = (SLABS) + 4 * kKC * 64; \
+        if ((L) <= kKC && (C) > 0.f)                                                        \
+            attend16<T, true, kWaves, 1, RT, 1>(QH, KH, VH, OH, R, L, LP, C, G_, GG, sK_, sV_, sQ_, \
+                                                CLS);                                        \
+        else if ((L) <= kKC)                                                                \
+            attend16<T, false, kWaves, 1, RT, 1>(QH, KH, VH, OH, R, L, LP, C, G_, GG, sK_, sV_, sQ_, \
+                                                 CLS);                                       \
+        else if ((C) > 0.f)                                                                 \
+            attend16_split<T, true>(QH, KH, VH, OH, R, L, LP, C, G_, GG, SLABS, CLS);        \
+        else                                                                                \
+            attend16_split<T, false>(QH, KH, VH, OH, R, L, LP, C, G_, GG, SLABS, CLS);       \
+    } while (0)
+
+// rattn_forward for batches of few heads
+template <typename T>
+__global__ __launch_bounds__(kThreads) void attn_fwd16s(const uint16_t *__restrict__ q,
+                                                        const uint16_t *__restrict__ k,
+                                                        const uint16_t *__restrict__ v,
+                                                        uint16_t *__restrict__ o,
+                                                        const int32_t *__restrict__ cu, int B,
+                                                        int H, int G, int max_seqlen, float c) {
+    __shared__ __attribute__((aligned(16))) uint16_t slabs[kWaves * kSlab16];
+    int b, h, g;
+    if (!decode_group(B * H, H, G, &b, &h, &g)) return;
+    const int seq0 = cu[b];
+    const int L = cu[b + 1] - seq0;
+    if (L <= 0 || L > max_seqlen) return;
+    const int64_t rs = (int64_t)H * kD;
+    const int64_t base = (int64_t)seq0 * rs + (int64_t)h * kD;
+    const FlatRows R = {(uint32_t)rs};
+    RATTN_ATTEND_FEW(FlatRows, q + base, k + base, v + base, o + base, R, L, L, c, g, G, slabs,
+                     nullptr);
+}
+
+// rattn_fused for batches of few heads
+template <typename T>
+__global__ __launch_bounds__(kThreads) void fused16s(const uint16_t *__restrict__ q,
+                                                     const uint16_t *__restrict__ k,
+                                                     const uint16_t *__restrict__ v,
+                                                     const uint8_t *__restrict__ keep,
+                                                     uint16_t *__restrict__ out,
+                                                     uint16_t *__restrict__ cls, int B, int N,
+                                                     int H, int G, int pad, float c) {
+    __shared__ __attribute__((aligned(16))) uint16_t slabs[kWaves * kSlab16];
+    __shared__ int16_t pos[kMaxFusedN];
+    __shared__ uint64_t keep_bits[kMaxFusedN / 64];
+    int b, h, g;
+    if (!decode_group(B * H, H, G, &b, &h, &g)) return;
+    const uint8_t *keep_img = keep + (int64_t)b * N;
+    const int L = rank_image<kWaves>(keep_img, N, pos, keep_bits);
+    const int64_t rs = (int64_t)H * kD;
+    const int64_t head0 = (int64_t)b * N * rs + (int64_t)h * kD;
+    uint16_t *cls_head = cls ? cls + ((int64_t)b * H + h) * kD : nullptr;
+    uint16_t *out_head = out ? out + head0 : nullptr;
+    if (L > 0) {
+        const PaddedRows R = {(uint32_t)rs, pos};
+        uint16_t *cls_dst = (cls_head && pos[0] == 0) ? cls_head : nullptr;
+        const int Lp = max(L, pad);
+        int gg = g, GG = G;
+        bool run = true;
+        if (!out) {
+            // CLS rows only: the workgroup holding query tile 0 computes that
+            // tile alone
+            run = cls_dst && g == 0;
+            GG = (Lp + kQW - 1) / kQW;
+            gg = 0;
+        }
+        if (run)
+            RATTN_ATTEND_FEW(PaddedRows, q + head0, k + head0, v + head0, out_head, R, L, Lp, c, gg,
+                             GG, slabs, cls_dst);
+    }
+    // zeros for the pruned rows: by the last workgroup of the head, after its
+    // attention
+    if (g == G - 1)
+        zero_pruned<kD * 2 / 16, kThreads>(keep_bits, N, out_head ? (u32x4 *)out_head : nullptr,
+                                           rs * 2 / 16, (u32x4 *)cls_head);
+}
+#undef RATTN_ATTEND_FEW
+
+
 template <bool SPLIT>
 __global__ __launch_bounds__(kThreads) void fused32(const float *__restrict__ q,
                                                     const float *__restrict__ k,
@@ -1261,6 +1570,13 @@ hipError_t launch_fwd16(const AttnArgs &a, float c, hipStream_t s) {
 
 template <typename T>
 hipError_t launch_fwd16_shape(const AttnArgs &a, float c, hipStream_t s) {
+    if (split16(a.B, a.H)) {
+        const int G = split_groups(a.B, a.H, a.max_seqlen, false);
+        return launch<attn_fwd16s<T>>(dim3((unsigned)grid_for(a.B, a.H, G)), dim3(kThreads), s,
+                                      (const uint16_t *)a.q, (const uint16_t *)a.k,
+                                      (const uint16_t *)a.v, (uint16_t *)a.o, a.cu, a.B, a.H, G,
+                                      a.max_seqlen, c);
+    }
     const Shape sh = shape_for(a.max_seqlen);
     if (sh.QB == 1) return launch_fwd16<T, 4, 1>(a, c, s);
     return launch_fwd16<T, 4, 2>(a, c, s);
@@ -1279,6 +1595,14 @@ hipError_t launch_fused16(const FusedArgs &a, float c, hipStream_t s) {
 
 template <typename T>
 hipError_t launch_fused16_shape(const FusedArgs &a, float c, hipStream_t s) {
+    if (split16(a.B, a.H)) {
+        // without the padded output only tile 0 (the CLS row) is computed
+        const int G = a.out ? split_groups(a.B, a.H, std::min(a.max_seqlen, a.N), true) : 1;
+        return launch<fused16s<T>>(dim3((unsigned)grid_for(a.B, a.H, G)), dim3(kThreads), s,
+                                   (const uint16_t *)a.q, (const uint16_t *)a.k,
+                                   (const uint16_t *)a.v, a.keep, (uint16_t *)a.out,
+                                   (uint16_t *)a.cls, a.B, a.N, a.H, G, a.pad, c);
+    }
     // the CLS-only mode computes one tile per head: the smallest workgroup
     const Shape sh = a.out ? shape_for(std::min(a.max_seqlen, a.N)) : Shape{4, 1};
     if (sh.QB == 1) return launch_fused16<T, 4, 1>(a, c, s);
@@ -1294,7 +1618,7 @@ hipError_t launch_attention(const AttnArgs &a, hipStream_t s) {
     case Elem::F16: return launch_fwd16_shape<_Float16>(a, c, s);
     case Elem::F32: {
         const bool split = split32(a.B, a.H);
-        const int G = split ? split32_groups(a.B, a.H, a.max_seqlen, false)
+        const int G = split ? split_groups(a.B, a.H, a.max_seqlen, false)
                             : tile_groups(a.B, a.H, a.max_seqlen, kQT, false);
         const dim3 grid((unsigned)grid_for(a.B, a.H, G));
         if (split)
@@ -1319,7 +1643,7 @@ hipError_t launch_fused(const FusedArgs &a, hipStream_t s) {
         // without the padded output only tile 0 (the CLS row) is computed
         const int bound = std::min(a.max_seqlen, a.N);
         const int G = !a.out ? 1
-                      : split ? split32_groups(a.B, a.H, bound, true)
+                      : split ? split_groups(a.B, a.H, bound, true)
                               : tile_groups(a.B, a.H, bound, kQT, true);
         const dim3 grid((unsigned)grid_for(a.B, a.H, G));
         if (split)

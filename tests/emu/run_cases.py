@@ -197,6 +197,31 @@ def case_padded():
               flush=True)
 
 
+def case_seq16():
+    # 16-bit batches of more than 24 heads run one wavefront per 16 query rows
+    # over all key chunks (fewer heads split long images' keys over the four
+    # wavefronts, which the other 16-bit cases run): 25 one-head images, most
+    # of one token, so that only a few are long.  N = 300 selects 128-row
+    # tiles (the 290-token image's third tile takes its chunks in reverse),
+    # N = 200 64-row tiles streaming four chunks.
+    for dt, N, long in (("bf16", 300, [290, 130, 65, 64, 0]), ("f16", 200, [200, 129, 65, 17, 0])):
+        keep = _keep_lengths(long + [1] * 20, N, seed=70 + N)
+        w = workloads.custom(25, N, 1, dt, keep=keep, seed=71 + N, name=f"seq16_{dt}_{N}")
+        check_both(w, flat=False)
+        if N != 200:
+            continue
+        # the padded comparator on this core: every image at N (the cheaper case)
+        ref_out, ref_cls = fused(w)
+        out = torch.empty_like(w.q)
+        cls = torch.empty((w.B, w.H, w.D), dtype=w.q.dtype)
+        for t in (out, cls):
+            t.view(torch.uint8).fill_(POISON)
+        rv.rattn_fused_padded(w.q, w.k, w.v, w.keep, w.scale, w.N, out_padded=out, cls=cls)
+        assert np.array_equal(U.bits(out), U.bits(ref_out)), (w.name, "padded out")
+        assert np.array_equal(U.bits(cls), U.bits(ref_cls)), (w.name, "padded cls")
+        print(f"{w.name}: padded to {w.N}: bits equal to ragged", flush=True)
+
+
 def case_f32_sequential():
     # float32 batches of more than 64 heads keep one wavefront per 16 query
     # rows over all key chunks (fewer heads split the keys over the four

@@ -11,7 +11,9 @@ kept counts.  rattn_pack does not run here.  Checked:
 * rows past T are left untouched;
 * the output is bitwise the fused kernel's output gathered at the kept
   positions, since both run the same attention core;
-* the bits do not depend on the max_seqlen bound, the run, or other images;
+* the bits do not depend on the max_seqlen bound, the run, or the other
+  images' contents; the batch's head count picks the core (up to 24 heads,
+  images longer than one chunk split their keys over the wavefronts);
 * an image longer than max_seqlen breaks the contract and is left unwritten.
 
 The five named workloads run at full size with max_seqlen = N, the launch
@@ -239,18 +241,41 @@ def test_forward_bound_across_tile_shapes_does_not_change_bits():
     assert np.array_equal(bits(a), bits(b))
 
 
-def test_forward_batch_equals_images_one_by_one():
-    # rows past 256 take the key chunks in reverse; the batch and one image
-    # alone split the heads over workgroups differently.  Same bits.
-    w = workloads.custom(32, 400, 8, "bf16", keep=_keep_length_range(32, 400, 260, 380, 62),
-                         seed=63, name="fwd_batch_vs_single")
+@pytest.mark.parametrize("B,H,picks", [(8, 32, (0, 3, 7)), (3, 8, (0, 1, 2))],
+                         ids=["many_heads", "few_heads"])
+def test_forward_batch_equals_images_one_by_one(B, H, picks):
+    # the core depends on the batch's head count (up to 24 heads, images
+    # longer than one chunk split their keys over the wavefronts); on the
+    # same side of that line a batch and its images alone split the heads over
+    # workgroups differently and give the same bits (rows past 256 take the
+    # key chunks in reverse)
+    w = workloads.custom(B, 400, H, "bf16", keep=_keep_length_range(B, 400, 260, 380, 62),
+                         seed=63, name=f"fwd_batch_vs_single_{B}x{H}")
     flat, cu = host_flat(w)
-    say("256-head batch vs images one by one, N=400, kept 260..380")
+    say(f"{B * H}-head batch vs images one by one, N=400, kept 260..380")
     o, T = run_forward(w, flat_cu=(flat, cu))
-    for b in (0, 7, 31):
+    for b in picks:
         s, e = int(cu[b]), int(cu[b + 1])
-        one = workloads.custom(1, 400, 8, "bf16", keep=w.keep[b:b + 1].clone(), seed=63,
+        one = workloads.custom(1, 400, H, "bf16", keep=w.keep[b:b + 1].clone(), seed=63,
                                name=f"fwd_single_{b}")
+        one.q, one.k, one.v = (t[b:b + 1].clone() for t in (w.q, w.k, w.v))
+        o1, T1 = run_forward(one)
+        assert T1 == e - s
+        assert np.array_equal(bits(o1[:T1]), bits(o[s:e])), b
+
+
+def test_forward_one_chunk_images_same_bits_at_any_head_count():
+    # images of at most 64 kept tokens run the same core in a batch of many
+    # heads (256) and alone (8 heads)
+    w = workloads.custom(32, 197, 8, "bf16", keep=_keep_length_range(32, 197, 1, 64, 64),
+                         seed=65, name="fwd_one_chunk_batch")
+    flat, cu = host_flat(w)
+    say("256-head batch of one-chunk images vs images one by one")
+    o, T = run_forward(w, flat_cu=(flat, cu))
+    for b in (0, 13, 31):
+        s, e = int(cu[b]), int(cu[b + 1])
+        one = workloads.custom(1, 197, 8, "bf16", keep=w.keep[b:b + 1].clone(), seed=65,
+                               name=f"fwd_one_chunk_{b}")
         one.q, one.k, one.v = (t[b:b + 1].clone() for t in (w.q, w.k, w.v))
         o1, T1 = run_forward(one)
         assert T1 == e - s

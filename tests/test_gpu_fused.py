@@ -7,8 +7,11 @@ kept rows, gathered in (b, n) order, match the oracle's attention within the
 tolerances of `_gpu_util` (fp32 1e-4, fp16 2e-3, bf16 1e-2 max-abs on
 unit-normal inputs; the 384 px workload against the derived rounding bound);
 CLS rows are bitwise the output rows (b, 0); results do not depend on the
-max_seqlen bound, on the contents of pruned input rows, on other images, or on
-the run.  The five named workloads run at full size in the launch
+max_seqlen bound, on the contents of pruned input rows, on other images'
+contents, or on the run (the batch's head count picks the core: up to 24
+heads, images longer than one chunk split their keys over the wavefronts, and
+a batch and its images alone agree bitwise on either side of that line).  The
+five named workloads run at full size in the launch
 configuration the benchmark times (max_seqlen = N); at the two largest the
 oracle computes sampled rows one by one.
 """
@@ -219,17 +222,39 @@ def test_fused_bound_across_tile_shapes_does_not_change_bits():
     assert np.array_equal(bits(a[0]), bits(b[0])) and np.array_equal(bits(a[1]), bits(b[1]))
 
 
-def test_fused_batch_equals_images_one_by_one():
-    # 256 heads: one workgroup per head, whose later tiles take the key
-    # chunks of rows past 256 in reverse and reuse the double buffer's chunks;
-    # one image alone: a workgroup per tile, no reuse.  Same bits.
-    w = workloads.custom(32, 400, 8, "bf16", keep=_keep_length_range(32, 400, 260, 380, 62),
-                         seed=63, name="batch_vs_single")
-    say("256-head batch vs images one by one, N=400, kept 260..380")
+@pytest.mark.parametrize("B,H,picks", [(8, 32, (0, 3, 7)), (3, 8, (0, 1, 2))],
+                         ids=["many_heads", "few_heads"])
+def test_fused_batch_equals_images_one_by_one(B, H, picks):
+    # The core depends on the batch's head count: up to 24 heads an image
+    # longer than one 64-key chunk has its keys split over a workgroup's
+    # wavefronts.  A batch and its images alone on the same side of that line
+    # give the same bits.  Many heads (256 in the batch): one workgroup per
+    # head, whose later tiles take the key chunks of rows past 256 in reverse
+    # and reuse the double buffer's chunks; an image alone: a workgroup per
+    # tile, no reuse.  Few heads: different numbers of workgroups per head.
+    w = workloads.custom(B, 400, H, "bf16", keep=_keep_length_range(B, 400, 260, 380, 62),
+                         seed=63, name=f"batch_vs_single_{B}x{H}")
+    say(f"{B * H}-head batch vs images one by one, N=400, kept 260..380")
     out, cls = run_fused(w)
-    for b in (0, 7, 31):
-        one = workloads.custom(1, 400, 8, "bf16", keep=w.keep[b:b + 1].clone(), seed=63,
+    for b in picks:
+        one = workloads.custom(1, 400, H, "bf16", keep=w.keep[b:b + 1].clone(), seed=63,
                                name=f"single_{b}")
+        one.q, one.k, one.v = (t[b:b + 1].clone() for t in (w.q, w.k, w.v))
+        o1, c1 = run_fused(one)
+        assert np.array_equal(bits(o1[0]), bits(out[b])), b
+        assert np.array_equal(bits(c1[0]), bits(cls[b])), b
+
+
+def test_fused_one_chunk_images_same_bits_at_any_head_count():
+    # images of at most 64 kept tokens run the same core in a batch of many
+    # heads (256) and alone (8 heads, a batch of few)
+    w = workloads.custom(32, 197, 8, "bf16", keep=_keep_length_range(32, 197, 1, 64, 64),
+                         seed=65, name="one_chunk_batch")
+    say("256-head batch of one-chunk images vs images one by one")
+    out, cls = run_fused(w)
+    for b in (0, 13, 31):
+        one = workloads.custom(1, 197, 8, "bf16", keep=w.keep[b:b + 1].clone(), seed=65,
+                               name=f"one_chunk_{b}")
         one.q, one.k, one.v = (t[b:b + 1].clone() for t in (w.q, w.k, w.v))
         o1, c1 = run_fused(one)
         assert np.array_equal(bits(o1[0]), bits(out[b])), b

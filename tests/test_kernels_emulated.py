@@ -70,6 +70,10 @@ def test_emulated_tiny_fp32(emu_lib):
     _run(emu_lib, "tiny")
 
 
+def test_emulated_16bit_sequential_cores(emu_lib):
+    _run(emu_lib, "seq16")
+
+
 def test_emulated_f32_sequential_core(emu_lib):
     _run(emu_lib, "f32_sequential")
 
