@@ -26,9 +26,14 @@ EXT_SOURCE = "pymod.c"
 # v5), so a wavefront's first addresses do not wait for a scalar load of the
 # argument segment.  Each kernel keeps a prologue that loads them itself when
 # the firmware does not preload.  Measured on MI355X, rattn_fused at DeiT-S:
-# 5.90 -> 5.65 us warm, 9.24 -> 8.9-9.0 us cold, bits unchanged.
+# 5.90 -> 5.65 us warm, 9.24 -> 8.9-9.0 us cold, bits unchanged.  Matrix
+# instructions write ordinary VGPRs (-amdgpu-mfma-vgpr-form): without it the
+# compiler gave the float32 kernels and the few-heads 16-bit kernels 16-36
+# accumulation registers and 72-582 copies between them and the VGPRs that
+# the softmax reads; the other kernels are unchanged by it.
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
-                "-packed-fp32-ops", "-mllvm", "-amdgpu-kernarg-preload-count=16"]
+                "-packed-fp32-ops", "-mllvm", "-amdgpu-kernarg-preload-count=16",
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def hipcc() -> str:
