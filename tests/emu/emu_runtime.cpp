@@ -7,9 +7,9 @@ thread_local unsigned emu_phase;
 EmuBlock *g_emu;
 void emu_launch(dim3 grid, dim3 block, const std::function<void()> &body) {
     const int nt = block.x;
-    std::barrier<> bb(nt);
-    std::vector<std::barrier<> *> wb;
-    for (int w = 0; w < nt / 64; ++w) wb.push_back(new std::barrier<>(64));
+    EmuBarrier bb(nt);
+    std::vector<EmuBarrier *> wb;
+    for (int w = 0; w < nt / 64; ++w) wb.push_back(new EmuBarrier(64));
     EmuBlock e; e.nthreads = nt; e.block_bar = &bb; e.wave_bar = wb;
     e.slot.assign(nt / 64, std::vector<uint64_t>(128));
     g_emu = &e;

@@ -37,10 +37,30 @@ extern thread_local emu_idx threadIdx, blockIdx;
 extern thread_local dim3 blockDim, gridDim;
 using std::min; using std::max;
 
+// Barrier for the emulation's lane threads, which far outnumber the host's
+// CPUs: a waiter spins briefly, then yields its CPU to the threads it waits
+// for (cheaper here than sleeping on a futex and being woken per arrival).
+struct EmuBarrier {
+    explicit EmuBarrier(int n) : n_(n) {}
+    void arrive_and_wait() {
+        const unsigned g = gen_.load(std::memory_order_acquire);
+        if (count_.fetch_add(1, std::memory_order_acq_rel) == n_ - 1) {
+            count_.store(0, std::memory_order_relaxed);
+            gen_.fetch_add(1, std::memory_order_acq_rel);
+            return;
+        }
+        for (int spin = 0; gen_.load(std::memory_order_acquire) == g; ++spin)
+            if (spin > 16) std::this_thread::yield();
+    }
+    int n_;
+    std::atomic<int> count_{0};
+    std::atomic<unsigned> gen_{0};
+};
+
 struct EmuBlock {
     int nthreads;
-    std::barrier<> *block_bar;
-    std::vector<std::barrier<> *> wave_bar;
+    EmuBarrier *block_bar;
+    std::vector<EmuBarrier *> wave_bar;
     std::vector<std::vector<uint64_t>> slot;      // per wave, 2 x 64 lanes, generic 8-byte payload
 };
 extern EmuBlock *g_emu;
