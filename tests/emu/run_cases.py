@@ -220,6 +220,17 @@ def case_seq16():
         assert np.array_equal(U.bits(out), U.bits(ref_out)), (w.name, "padded out")
         assert np.array_equal(U.bits(cls), U.bits(ref_cls)), (w.name, "padded cls")
         print(f"{w.name}: padded to {w.N}: bits equal to ragged", flush=True)
+    # the exact bound (250) selects 64-row tiles, N = 300 128-row tiles: same bits
+    keep = _keep_lengths([250, 200, 129, 64, 0] + [1] * 20, 300, seed=72)
+    w = workloads.custom(25, 300, 1, "bf16", keep=keep, seed=73, name="seq16_shapes")
+    a = three_call(w, max_seqlen=max(w.kept_counts))
+    b = three_call(w)
+    assert np.array_equal(U.bits(a["po"]), U.bits(b["po"])), "tile shape changed bits"
+    fa, _ = fused(w, max_seqlen=max(w.kept_counts))
+    fb, _ = fused(w)
+    assert np.array_equal(U.bits(fa), U.bits(fb)), "tile shape changed fused bits"
+    print("seq16_shapes: max_seqlen 250 (64-row tiles) / 300 (128-row tiles): same bits",
+          flush=True)
 
 
 def case_f32_sequential():
