@@ -720,6 +720,72 @@ def config_workload(spec: str, seed):
         raise SystemExit(f"unknown --config {name}") from None
 
 
+COLD_TRACE_LAUNCHES = 20
+
+
+def cold_trace_target(spec: str) -> None:
+    """Launches for a kernel trace of cold single launches (run under
+    rocprofv3 --kernel-trace): on one workload, COLD_TRACE_LAUNCHES launches of
+    rattn_fused, each right after `evict_caches` on the same stream with no
+    events around them, then as many back to back; then the same for
+    rattn_forward on its flat buffers.  The trace gives each launch's own
+    duration, measured without host events."""
+    w = config_workload(spec, None)
+    rattn_init()
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device="cuda")
+    r = Resident(w, stream)
+    f = FlatResident(w, stream)
+    step = f.c_step()
+    lib = timing_lib()
+
+    def forward():
+        if lib.bench_loop(ctypes.byref(step), WHAT_FORWARD, 1) != 0:
+            raise RuntimeError("bench_loop(forward) failed")
+
+    for launch in (r.step, forward):
+        launch()
+        torch.cuda.synchronize()
+        for _ in range(COLD_TRACE_LAUNCHES):
+            evict_caches(flush)
+            launch()
+        torch.cuda.synchronize()
+        # the same kernel back to back, for the trace's own warm figure
+        for _ in range(COLD_TRACE_LAUNCHES + 1):
+            launch()
+        torch.cuda.synchronize()
+    print(f"[bench] cold trace target {w.name}: {COLD_TRACE_LAUNCHES} cold and "
+          f"{COLD_TRACE_LAUNCHES} back-to-back launches each of rattn_fused and rattn_forward",
+          flush=True)
+
+
+def summarize_cold_trace(trace_csv: str) -> str:
+    """Summary text of a rocprofv3 kernel trace of `bench.py --cold-trace`,
+    per attention kernel: the durations of the launches that directly follow
+    the cache eviction's reduction kernel (cold), and of those that directly
+    follow a launch of the same kernel (warm, back to back)."""
+    import csv
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    runs = {}
+    for prev, row in zip(rows, rows[1:]):
+        name = row["Kernel_Name"]
+        if "fused16" not in name and "attn_fwd16" not in name:
+            continue
+        kind = ("cold" if "reduce" in prev["Kernel_Name"]
+                else "warm" if prev["Kernel_Name"] == name else None)
+        if kind:
+            us = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1000.0
+            runs.setdefault((kind, name), []).append(us)
+    if not any(kind == "cold" for kind, _ in runs):
+        raise RuntimeError("no cold attention launches in the trace")
+    out = []
+    for (kind, name), us in runs.items():
+        us.sort()
+        out.append(f"{kind} launches {len(us)} median_us {us[len(us) // 2]:.2f} "
+                   f"min_us {us[0]:.2f} max_us {us[-1]:.2f} kernel {name}")
+    return "\n".join(out) + "\n"
+
+
 STACK_WORKLOADS = {"deit_s_80pct": workloads.deit_s, "deit_b_384_50pct": workloads.deit_b_384,
                    "large_batch_threshold_l2": workloads.large_batch}
 
@@ -930,6 +996,11 @@ def main():
     ap.add_argument("--quick", action="store_true",
                     help="main metric only: no dispatch floors, no large configs, no CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-trace", metavar="NAME",
+                    help="only cold single launches of rattn_fused and rattn_forward on one "
+                         "workload (for rocprofv3 --kernel-trace), then exit")
+    ap.add_argument("--cold-summary", metavar="KERNEL_TRACE_CSV",
+                    help="summarize the cold launches in a kernel trace of --cold-trace")
     ap.add_argument("--pmc-target", action="store_true",
                     help="only the launches the traffic counters are read on, then exit")
     ap.add_argument("--pmc-forward", choices=["deit_s", "deit_b_384", "large_batch"],
@@ -959,6 +1030,12 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.cold_summary:
+        sys.stdout.write(summarize_cold_trace(args.cold_summary))
+        return
+    if args.cold_trace:
+        cold_trace_target(args.cold_trace)
+        return
     if args.pmc_target:
         pmc_target()
         return

@@ -242,3 +242,38 @@ def test_config_workload_names():
     for bad in ("nope", "deit_s:3", "deit_b_sweep:4"):
         with pytest.raises(SystemExit):
             bench.config_workload(bad, None)
+
+
+def test_cold_trace_summary_takes_the_launches_after_the_eviction(tmp_path):
+    """Attention launches that directly follow the eviction's reduction
+    kernel count as cold, those that follow a launch of the same kernel as
+    warm, the rest (after another kernel) as neither; each kernel gets its own
+    medians."""
+    fused = "void rattn::(anonymous namespace)::fused16<__bf16, 4, 2>(...)"
+    fwd = "void rattn::(anonymous namespace)::attn_fwd16<__bf16, 4, 2>(...)"
+    red = "void at::native::reduce_kernel<512, 1>(...)"
+    fill = "void at::native::vectorized_elementwise_kernel<4, FillFunctor>(...)"
+    seq = [(fused, 40), (fill, 9), (red, 30), (fused, 50), (fill, 9), (red, 30), (fused, 52),
+           (fill, 9), (red, 30), (fused, 54), (fused, 41), (fwd, 35), (fill, 9), (red, 30),
+           (fwd, 44)]
+    path = tmp_path / "trace.csv"
+    t = 1000
+    with open(path, "w", newline="") as f:
+        wr = csv.DictWriter(f, ["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        wr.writeheader()
+        # rows out of start order, as a trace may list them
+        rows = []
+        for name, us in seq:
+            rows.append({"Kernel_Name": name, "Start_Timestamp": t,
+                         "End_Timestamp": t + us * 1000})
+            t += us * 1000 + 500
+        for r in reversed(rows):
+            wr.writerow(r)
+    out = bench.summarize_cold_trace(str(path)).splitlines()
+    assert len(out) == 3
+    by = {(ln.split()[0], ln.split(" kernel ")[1]): ln.split() for ln in out}
+    f = by[("cold", fused)]
+    assert f[2] == "3" and f[4] == "52.00" and f[6] == "50.00" and f[8] == "54.00"
+    assert by[("warm", fused)][2:5] == ["1", "median_us", "41.00"]
+    w = by[("cold", fwd)]
+    assert w[2] == "1" and w[4] == "44.00"
