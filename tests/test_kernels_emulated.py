@@ -3,7 +3,8 @@
 api.hip, pack.hip and attention.hip are compiled for x86 by clang++ against the
 emulation shim in tests/emu (one host thread per lane, wave intrinsics, MFMA,
 global_load_lds and the transposing LDS read emulated from their documented or
-measured lane layouts) with AddressSanitizer, and driven through the Python
+measured lane layouts) with AddressSanitizer and UndefinedBehaviorSanitizer
+(signed overflow, shifts, invalid loads, division; any report aborts), and driven through the Python
 binding and the C ABI on host tensors.  Every entry point is checked:
 rattn_pack, rattn_forward and rattn_unpack against the oracle (the scan and
 the row movement bit-exact, attention within the per-dtype tolerances of
@@ -44,8 +45,8 @@ def emu_lib(tmp_path_factory):
     out = str(tmp_path_factory.mktemp("emu") / "librattn_emu.so")
     # RATTN_LAUNCH_GGL: the emulated runtime runs a kernel as a function call
     # (hipLaunchKernelGGL), not through a device function handle
-    cmd = [CLANG, "-std=c++20", "-O1", "-g", "-fPIC", "-shared", "-fsanitize=address",
-           "-shared-libasan", "-fno-omit-frame-pointer", "-w", "-DRATTN_LAUNCH_GGL",
+    cmd = [CLANG, "-std=c++20", "-O1", "-g", "-fPIC", "-shared", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=undefined", "-shared-libasan", "-fno-omit-frame-pointer", "-w", "-DRATTN_LAUNCH_GGL",
            "-I", os.path.join(HERE, "emu"), "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            "-x", "c++", os.path.join(HERE, "emu", "emu_runtime.cpp"),
            os.path.join(CSRC, "api.hip"), os.path.join(CSRC, "pack.hip"),
